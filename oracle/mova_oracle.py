@@ -1,0 +1,175 @@
+"""Float64 CPU oracle of the MoVA routed value projection.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.  It shares no code with
+the HIP path.
+
+What is computed, and where it is stated
+----------------------------------------
+Page "MoVA: routing the value vectors, and why the KV cache does not notice",
+section "Where the routing happens", shows the attention layer's value path:
+
+1. router logits are a bias-free linear map of the token (the router's weight
+   only) from width d to E experts;
+2. the logits go through a sigmoid and the router's bias is handed to the
+   weight computation separately; the four (k) top experts are kept and their
+   sigmoid scores are renormalised to sum to one and multiplied by 2.5;
+3. each kept expert is a full d -> 8*128 linear map (no bias), SiLU is applied
+   to each expert's output, and the k results are summed with the weights;
+4. the (tokens, 1024) result is viewed as (tokens, 8, 128), column n being
+   head n // 128, lane n % 128 -- the shape of a plain GQA value projection.
+
+The same page's section "So what does it cost?" says the released combine is
+a loop with one gather / project / index-add per touched expert;
+``combine_experts`` follows that loop (it is the plainest correct order, not
+a design for speed).  Matrix products use numpy's float64 matmul.
+
+Readings where the pages leave a step open
+------------------------------------------
+* Bias role (parity unpinned).  The code passes the router bias separately
+  from the linear map, and the page describes the weights as the kept
+  experts' sigmoid scores divided by their sum and multiplied by 2.5.  The
+  default reading ("select") adds the bias to the sigmoid
+  scores for choosing experts only and weighs with the unbiased scores.  Two
+  alternatives are kept for documentation: "logit" (sigmoid of logit + bias
+  for both) and "weights" (biased scores used as weights too).
+* Ties: equal selection scores go to the lower expert index, and the k
+  selected experts are returned in order of (score desc, index asc).
+* No epsilon in the renormalisation (k sigmoid values are each > 0).
+* Experts have no bias: 64 * 2560 * 1024 * 45 = 7,549,747,200 value-expert
+  parameters is the page's exact count, leaving no room for one.
+* Router summation order (parity unpinned): float64 here; any fixed order is
+  acceptable, near-ties are handled by the margin rule in the tests.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BIAS_ROLES = ("select", "logit", "weights")
+
+
+def _f64(a) -> np.ndarray:
+    """Upcast anything array-like (numpy, or torch via .numpy()) to float64."""
+    if hasattr(a, "detach"):  # a torch tensor: go through float64 on the CPU
+        a = a.detach().to("cpu").double().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """Logistic function 1 / (1 + e^-z) in float64."""
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU z * sigmoid(z) (F.silu in the quoted code)."""
+    return z * sigmoid(z)
+
+
+def router_logits(x, router_w) -> np.ndarray:
+    """Logits [T, E] = x [T, d] @ router_w[E, d]^T, the router's weight only
+    (section "Where the routing happens": the linear map takes
+    ``v_router.weight`` and no bias)."""
+    return _f64(x) @ _f64(router_w).T
+
+
+@dataclasses.dataclass
+class Routing:
+    """Per-token routing decision.
+
+    idx [T, k] int64: selected experts ordered by (sel desc, index asc).
+    w   [T, k] float64: renormalised scores times ``scale``.
+    s   [T, E] float64: sigmoid scores.  sel [T, E]: selection scores.
+    margin [T]: k-th largest minus (k+1)-th largest selection score
+    (+inf when k == E).
+    """
+
+    idx: np.ndarray
+    w: np.ndarray
+    s: np.ndarray
+    sel: np.ndarray
+    margin: np.ndarray
+
+
+def route(x, router_w, router_b, k: int, scale: float = 2.5,
+          bias_role: str = "select") -> Routing:
+    """Sigmoid router, top-k and renormalised weights.
+
+    Page "MoVA: routing the value vectors ...", section "Where the routing
+    happens": sigmoid scoring, top_k=4, scaling_factor=2.5; the weights are the
+    kept experts' scores divided by their sum, times 2.5.  ``bias_role`` selects the
+    reading of where the router bias enters (module docstring).
+    """
+    if bias_role not in BIAS_ROLES:
+        raise ValueError(f"bias_role must be one of {BIAS_ROLES}")
+    logits = router_logits(x, router_w)
+    T, E = logits.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    b = np.zeros(E) if router_b is None else _f64(router_b).reshape(E)
+    if bias_role == "logit":
+        s = sigmoid(logits + b)
+        sel = s
+    else:
+        s = sigmoid(logits)
+        sel = s + b
+    # Order experts by selection score, descending, lower index first on ties.
+    expert_ids = np.broadcast_to(np.arange(E), (T, E))
+    order = np.lexsort((expert_ids, -sel), axis=1)
+    idx = order[:, :k]
+    ranked = np.take_along_axis(sel, order, axis=1)
+    margin = ranked[:, k - 1] - ranked[:, k] if k < E else np.full(T, np.inf)
+    chosen = np.take_along_axis(sel if bias_role == "weights" else s, idx, axis=1)
+    w = scale * chosen / chosen.sum(axis=1, keepdims=True)
+    return Routing(idx=idx, w=w, s=s, sel=sel, margin=margin)
+
+
+def combine_experts(x, expert_w, idx, w) -> np.ndarray:
+    """out [T, N] = sum_j w[t, j] * SiLU(W_{idx[t, j]} x_t).
+
+    The released combine's loop (section "So what does it cost?"): for every
+    touched expert, gather the tokens that chose it, apply that expert's
+    linear map, SiLU, scale each row by its routing weight and index-add the
+    rows into the output.
+    """
+    x = _f64(x)
+    W = _f64(expert_w)
+    idx = np.asarray(idx)
+    w = _f64(w)
+    T = x.shape[0]
+    N = W.shape[1]
+    out = np.zeros((T, N))
+    for e in np.unique(idx):
+        rows, slots = np.nonzero(idx == e)
+        z = x[rows] @ W[e].T
+        contrib = w[rows, slots][:, None] * silu(z)
+        np.add.at(out, rows, contrib)
+    return out
+
+
+def value_forward(x, router_w, router_b, expert_w, k: int, scale: float = 2.5,
+                  n_kv_heads: Optional[int] = None, head_dim: int = 128,
+                  bias_role: str = "select"):
+    """Full value path: routing, expert combine, GQA view.
+
+    Returns (out [T, n_kv_heads, head_dim] float64, Routing).  The view puts
+    column n at head n // head_dim, lane n % head_dim ("Where the routing
+    happens": ``view(..., -1, 128)``).
+    """
+    r = route(x, router_w, router_b, k, scale, bias_role)
+    out = combine_experts(x, expert_w, r.idx, r.w)
+    N = out.shape[1]
+    if n_kv_heads is None:
+        n_kv_heads = N // head_dim
+    if n_kv_heads * head_dim != N:
+        raise ValueError("n_kv_heads * head_dim must equal the expert width")
+    return out.reshape(out.shape[0], n_kv_heads, head_dim), r
+
+
+def dense_value_proj(x, w_v) -> np.ndarray:
+    """Plain GQA value projection V = x W_v^T (the dense layers' v_proj, section
+    "So what does it cost?"), float64."""
+    return _f64(x) @ _f64(w_v).T
