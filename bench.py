@@ -1,0 +1,241 @@
+"""Benchmark of the MoVA routed value projection on one MI355X.
+
+A step is one mova_value_forward call (router, dispatch, expert projection,
+combine) on one batch of seeded synthetic tokens with inputs already resident
+in HBM.  The headline workload is the decode step (T=64, d=2560, 64 experts
+of 2560->1024, top-4, bf16); the prefill workloads (T=4096 chunk, T=32768
+skewed, 8x8192 chunked through 4 layers) are measured as secondary lines in
+the same JSON object unless --headline-only is given.
+
+Layer weights are rotated over several copies (>= 1.3 GB in total) so the
+256 MB Infinity Cache cannot serve them between steps.
+
+Prints ONE JSON line.  Algorithmic work: 2*(k*d*N + d*E) FLOP per token;
+bytes = touched experts' weights once + router weights + x + out.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from mixture_value_projection_amd import accounting, binding, inputs  # noqa: E402
+
+METRIC = "MoVA value-proj tokens/sec + % bf16 MFMA peak (prefill) / % HBM BW (decode)"
+DEV = "cuda:0"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_copies(shape, seed, dtype, bias, n_copies, layer=0):
+    """n_copies device copies of one layer's weights (same values, distinct memory)."""
+    w = inputs.make_weights(shape, seed, dtype, bias, layer)
+    base = {k: v.to(DEV) for k, v in w.items()}
+    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(n_copies - 1)]
+    return copies
+
+
+def timed_calls(calls, steps, warmup, stage):
+    """Run warmup + steps calls; returns (seconds for the steps, stage ms avg)."""
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    binding.timing_enable(steps * 64, stages=(stage,))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    rec = binding.timing_read()
+    binding.timing_enable(0)
+    tot, cnt = rec[binding.STAGES.index(stage)]
+    return t1 - t0, (tot / cnt if cnt else float("nan")), cnt
+
+
+def run_single_layer(name, steps, warmup, copies):
+    w = inputs.WORKLOADS[name]
+    sh = w.shape
+    x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
+    cps = make_copies(sh, w.seed, w.dtype, w.bias, copies)
+    out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty(sh.T, sh.k, dtype=torch.int32, device=DEV)
+    ws = torch.empty(binding.workspace_bytes(sh.T, sh.d, sh.E, sh.k, sh.n_kv_heads, sh.head_dim),
+                     dtype=torch.uint8, device=DEV)
+    binding.value_forward(x, cps[0]["router_w"], cps[0]["router_b"], cps[0]["expert_w"], sh.k,
+                          sh.scale, sh.n_kv_heads, sh.head_dim, out=out, topk_idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=sh.E)
+    touched = int((counts > 0).sum())
+
+    def mk(c):
+        return lambda: binding.value_forward(x, c["router_w"], c["router_b"], c["expert_w"], sh.k,
+                                             sh.scale, sh.n_kv_heads, sh.head_dim, out=out,
+                                             workspace=ws)
+    calls = [mk(c) for c in cps]
+    secs, stage_ms, nrec = timed_calls(calls, steps, warmup, "experts")
+    tokens = sh.T * steps
+    return dict(shape=sh, seconds=secs, tokens=tokens, calls=steps, stage_ms=stage_ms,
+                stage_records=nrec,
+                touched=touched, max_load=int(counts.max()), mean_load=float(counts.mean()))
+
+
+def run_chunked(steps, warmup):
+    """One step = the whole 65536-token stream through 4 layers (32 calls)."""
+    w = inputs.WORKLOADS["chunked"]
+    sh = w.shape
+    total = sh.T * w.chunks
+    x = inputs.make_tokens(total, sh.d, w.seed, w.dtype).to(DEV)
+    layers = [make_copies(sh, w.seed, w.dtype, w.bias, 1, layer=l)[0] for l in range(w.layers)]
+    outs = [torch.empty(total, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+            for _ in range(w.layers)]
+    ws = torch.empty(binding.workspace_bytes(sh.T, sh.d, sh.E, sh.k, sh.n_kv_heads, sh.head_dim),
+                     dtype=torch.uint8, device=DEV)
+
+    def step():
+        for c in range(w.chunks):
+            s = slice(c * sh.T, (c + 1) * sh.T)
+            for l, L in enumerate(layers):
+                binding.value_forward(x[s], L["router_w"], L["router_b"], L["expert_w"], sh.k,
+                                      sh.scale, sh.n_kv_heads, sh.head_dim, out=outs[l][s],
+                                      workspace=ws)
+    secs, stage_ms, nrec = timed_calls([step], steps, warmup, "experts")
+    return dict(shape=sh, seconds=secs, tokens=total * steps, layer_tokens=total * w.layers * steps,
+                calls=steps * w.chunks * w.layers, stage_ms=stage_ms, stage_records=nrec)
+
+
+def prefill_line(name, r):
+    sh = r["shape"]
+    fpt = accounting.flops_per_token(sh.d, sh.E, sh.k, sh.N)
+    layer_tokens = r.get("layer_tokens", r["tokens"])
+    tflops = layer_tokens * fpt / r["seconds"] / 1e12
+    per_call_tokens = sh.T
+    gemm_flops = 2 * per_call_tokens * sh.k * sh.d * sh.N
+    gemm_tflops = gemm_flops / (r["stage_ms"] * 1e-3) / 1e12
+    return {
+        "workload": name,
+        "tokens_per_s": r["tokens"] / r["seconds"],
+        "ms_per_call": 1e3 * r["seconds"] / r["calls"],
+        "tflops": tflops,
+        "frac_bf16_peak": tflops * 1e12 / accounting.BF16_MFMA_PEAK_FLOPS,
+        "grouped_gemm_us": 1e3 * r["stage_ms"],
+        "grouped_gemm_tflops": gemm_tflops,
+        "grouped_gemm_frac": gemm_tflops * 1e12 / accounting.BF16_MFMA_PEAK_FLOPS,
+    }
+
+
+def cpu_baseline(seconds_target=12.0):
+    """The CPU oracle on the decode workload's tokens, repeated for ~seconds_target."""
+    sys.path.insert(0, ROOT)
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    w = inputs.WORKLOADS["decode"]
+    sh = w.shape
+    t = inputs.make_layer(sh, w.seed, w.dtype, w.bias)
+    o = {k: v.double().numpy() for k, v in t.items()}
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.value_forward(o["x"], o["router_w"], o["router_b"], o["expert_w"], sh.k, sh.scale,
+                             sh.n_kv_heads, sh.head_dim)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= seconds_target:
+            break
+    return {"value": sh.T * calls / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"decode workload (T={sh.T}) evaluated {calls}x by the float64 numpy oracle, "
+                      f"{el:.1f} s, host {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
+    ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this library has no "
+              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    binding.load_library()
+    torch.cuda.set_device(0)
+
+    log("decode workload ...")
+    r = run_single_layer("decode", args.steps, args.warmup, args.copies)
+    sh = r["shape"]
+    step_s = r["seconds"] / args.steps
+    tok_s = r["tokens"] / r["seconds"]
+    call_bytes = accounting.bytes_per_call(sh.T, r["touched"], sh.d, sh.E, sh.N, sh.k)
+    kern_bytes = accounting.expert_kernel_bytes(sh.T, r["touched"], sh.d, sh.N)
+    achieved = kern_bytes / (r["stage_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * step_s,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode step: T=64 tokens, d=2560, E=64 experts 2560->1024 "
+                               "(8 KV heads x 128), top-4, scale 2.5, bf16, seeded synthetic "
+                               "inputs, 4 rotated weight copies",
+                   "T": sh.T, "d": sh.d, "E": sh.E, "k": sh.k, "n_kv_heads": sh.n_kv_heads,
+                   "head_dim": sh.head_dim, "touched_experts": r["touched"]},
+        "whole_call": {"GB_per_s": call_bytes / step_s / 1e9,
+                       "frac_hbm": call_bytes / step_s / accounting.HBM_PEAK_BPS,
+                       "bytes": call_bytes},
+        "roofline": {"kernel": "decode_kernel (expert weight stream)", "bound": "hbm",
+                     "achieved": achieved, "peak": accounting.HBM_PEAK_BPS / 1e9, "unit": "GB/s",
+                     "frac": achieved * 1e9 / accounting.HBM_PEAK_BPS, "traffic": None,
+                     "bytes_per_launch": kern_bytes, "avg_launch_us": 1e3 * r["stage_ms"],
+                     "launches_timed": r["stage_records"]},
+    }
+    if not args.headline_only:
+        sec = []
+        for name in ("prefill", "skewed"):
+            log(f"{name} workload ...")
+            rr = run_single_layer(name, max(5, args.steps // 10), max(2, args.warmup // 4),
+                                  args.copies if name == "prefill" else 2)
+            d = prefill_line(name, rr)
+            d["max_over_mean_load"] = rr["max_load"] / rr["mean_load"]
+            sec.append(d)
+            torch.cuda.empty_cache()
+        log("chunked workload ...")
+        rr = run_chunked(max(2, args.steps // 50), 1)
+        sec.append(prefill_line("chunked", rr))
+        line["secondary"] = sec
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

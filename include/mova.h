@@ -1,0 +1,136 @@
+/*
+ * mova.h -- C ABI of the MoVA routed value projection for MI355X (gfx950).
+ *
+ * MoVA replaces an attention layer's value projection with a router and E
+ * value experts (page "MoVA: routing the value vectors, and why the KV cache
+ * does not notice", section "Where the routing happens"): per token, logits
+ * = x Wr^T (router weight only), sigmoid scores, the k experts with the
+ * highest selection score are kept, their scores are divided by their sum and
+ * multiplied by `scale`, each kept expert's output goes through SiLU, and the
+ * weighted sum is one [n_kv_heads, head_dim] value vector per token -- the
+ * shape a plain GQA value projection produces.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers (HIP device memory), row-major
+ *   and contiguous, 16-byte aligned.  The caller owns every buffer; the
+ *   library never allocates, frees or synchronises device memory.
+ * - bf16 means IEEE bfloat16 stored in 2 bytes; float means IEEE fp32.
+ * - Work is enqueued asynchronously on `stream` (NULL = the null stream).
+ *   Calls are stateless: concurrent calls need distinct outputs and
+ *   workspaces.
+ * - Return value: MOVA_OK or a negative mova_status.  Argument errors are
+ *   detected on the host before anything is enqueued, so outputs are left
+ *   untouched.  A failed kernel launch returns MOVA_ERR_HIP.
+ * - T == 0 returns MOVA_OK and enqueues nothing.
+ * - Supported domain: 1 <= E <= 64, 1 <= k <= min(E, 8), d > 0 and
+ *   d % 64 == 0, N = n_kv_heads * head_dim with 0 < N <= 16384 and
+ *   N % 64 == 0, 0 <= T <= 2^24, scale finite.
+ *
+ * Reading of the router bias (the pages pass it separately and do not show
+ * where it enters): the bias is added to the sigmoid scores to choose the k
+ * experts; the weights are computed from the unbiased scores.  Ties in the
+ * selection score go to the lower expert index, and the k selected experts
+ * are reported in order of (selection score desc, index asc).
+ */
+#ifndef MOVA_H
+#define MOVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t; /* identical to hip_runtime_api.h */
+
+enum mova_status {
+  MOVA_OK = 0,
+  MOVA_ERR_INVALID_ARG = -1, /* null pointer, negative size, misaligned pointer */
+  MOVA_ERR_UNSUPPORTED = -2, /* shape outside the supported domain */
+  MOVA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than mova_workspace_bytes */
+  MOVA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+};
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int mova_version(void);
+
+/* Human-readable name of a status code; never NULL, static storage. */
+const char* mova_status_str(int status);
+
+/*
+ * Bytes of device workspace mova_value_forward needs for these sizes; 0 when
+ * T == 0, and (size_t)-1 when the sizes are outside the supported domain.
+ * Depends only on the sizes, never on the data.
+ */
+size_t mova_workspace_bytes(int T, int d, int E, int k, int n_kv_heads, int head_dim);
+
+/*
+ * Routing only: the router linear map, sigmoid, bias-for-selection, top-k,
+ * renormalisation and scaling (section "Where the routing happens": the
+ * router logits line and calc_router_weights with "sigmoid", top_k and
+ * scaling_factor).
+ *
+ *   x        bf16  [T, d]   tokens
+ *   router_w bf16  [E, d]   router weight (nn.Linear layout)
+ *   router_b float [E]      router bias, NULL = zeros
+ *   topk_idx int32 [T, k]   out: selected experts, ordered as above
+ *   topk_w   float [T, k]   out: weights, sum over k equals `scale`
+ *
+ * Logits are accumulated in fp32 from the bf16 products.
+ */
+int mova_route(const void* x, const void* router_w, const float* router_b,
+               int T, int d, int E, int k, float scale,
+               int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/*
+ * Full value projection (section "Where the routing happens": routing, then
+ * combine_routed_experts with F.silu, then the view as heads of 128):
+ *
+ *   out[t, h, j] = sum_{i<k} w[t,i] * SiLU( sum_c x[t,c] * expert_w[idx[t,i], h*head_dim + j, c] )
+ *
+ *   x            bf16  [T, d]
+ *   router_w     bf16  [E, d]
+ *   router_b     float [E]          NULL = zeros
+ *   expert_w     bf16  [E, N, d]    stacked bias-free experts, N = n_kv_heads*head_dim
+ *   out          bf16  [T, n_kv_heads, head_dim]   (= [T, N] row-major)
+ *   topk_idx_out int32 [T, k]       optional (NULL): the routing used
+ *   topk_w_out   float [T, k]       optional (NULL)
+ *   workspace    device scratch of at least mova_workspace_bytes(...) bytes,
+ *                256-byte aligned; its contents on entry do not matter.
+ *
+ * Expert products accumulate in fp32; SiLU, weighting and the k-way sum are
+ * fp32 in a fixed slot order (i = 0..k-1), rounded once to bf16 (nearest
+ * even).  Results are bitwise reproducible for identical inputs and do not
+ * depend on how the tokens are split across calls.
+ */
+int mova_value_forward(const void* x, const void* router_w, const float* router_b,
+                       const void* expert_w, int T, int d, int E, int k, float scale,
+                       int n_kv_heads, int head_dim, void* out,
+                       int32_t* topk_idx_out, float* topk_w_out,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Stage timing (profiling aid).  While enabled, each mova_value_forward call
+ * records a HIP event pair on the call's stream around each stage selected
+ * by `stage_mask` (bit s = stage s), for up to `capacity` calls.  Stages:
+ * 0 router, 1 dispatch, 2 expert projection (grouped GEMM or decode stream),
+ * 3 combine.
+ *
+ * mova_timing_enable(capacity, stage_mask) starts a new collection
+ * (capacity <= 0 or stage_mask == 0 turns timing off); it creates host-side
+ * HIP events, no device memory.
+ * mova_timing_read waits for the recorded events and writes, for stage s < n,
+ * the summed milliseconds to total_ms[s] and the number of recorded launches
+ * to count[s].  Returns MOVA_OK, MOVA_ERR_INVALID_ARG or MOVA_ERR_HIP.
+ * Not thread-safe with concurrent forward calls.
+ */
+int mova_timing_enable(int capacity, unsigned stage_mask);
+int mova_timing_read(int n, double* total_ms, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOVA_H */

@@ -1,0 +1,180 @@
+"""ctypes binding of ``libmova.so`` (the C ABI in include/mova.h).
+
+Argument marshalling only: torch tensors are checked (device, dtype, shape,
+contiguity), their device pointers and the current HIP stream are handed to
+the library, and a negative status becomes ``MovaError``.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Tuple
+
+import torch
+
+from .build import LIBPATH
+
+_LIB = None
+
+MOVA_OK = 0
+STAGES = ("router", "dispatch", "experts", "combine")
+
+
+class MovaError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        super().__init__(f"{what}: {status_str(rc)} ({rc})")
+        self.rc = rc
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmova.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    p = path or os.environ.get("MOVA_LIB", LIBPATH)
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m mixture_value_projection_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mova_version.restype = i
+    lib.mova_version.argtypes = []
+    lib.mova_status_str.restype = ctypes.c_char_p
+    lib.mova_status_str.argtypes = [i]
+    lib.mova_workspace_bytes.restype = sz
+    lib.mova_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mova_route.restype = i
+    lib.mova_route.argtypes = [vp, vp, vp, i, i, i, i, f, vp, vp, vp]
+    lib.mova_value_forward.restype = i
+    lib.mova_value_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, vp, vp, sz, vp]
+    lib.mova_timing_enable.restype = i
+    lib.mova_timing_enable.argtypes = [i, ctypes.c_uint]
+    lib.mova_timing_read.restype = i
+    lib.mova_timing_read.argtypes = [i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    _LIB = lib
+    return lib
+
+
+def status_str(rc: int) -> str:
+    return load_library().mova_status_str(int(rc)).decode()
+
+
+def version() -> int:
+    return load_library().mova_version()
+
+
+def workspace_bytes(T: int, d: int, E: int, k: int, n_kv_heads: int, head_dim: int) -> int:
+    n = load_library().mova_workspace_bytes(T, d, E, k, n_kv_heads, head_dim)
+    if n == ctypes.c_size_t(-1).value:
+        raise MovaError(-2, "mova_workspace_bytes")
+    return n
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...], device) -> None:
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def route(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor], k: int,
+          scale: float = 2.5, topk_idx: Optional[torch.Tensor] = None,
+          topk_w: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """mova_route: returns (idx int32 [T, k], w float32 [T, k])."""
+    lib = load_library()
+    T, d = x.shape
+    E = router_w.shape[0]
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(router_w, "router_w", torch.bfloat16, (E, d), dev)
+    if router_b is not None:
+        _check(router_b, "router_b", torch.float32, (E,), dev)
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    rc = lib.mova_route(_ptr(x), _ptr(router_w), _ptr(router_b), T, d, E, k, float(scale),
+                        _ptr(topk_idx), _ptr(topk_w), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_route")
+    return topk_idx, topk_w
+
+
+def value_forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
+                  expert_w: torch.Tensor, k: int, scale: float = 2.5,
+                  n_kv_heads: Optional[int] = None, head_dim: int = 128,
+                  out: Optional[torch.Tensor] = None,
+                  topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mova_value_forward: returns out bf16 [T, n_kv_heads, head_dim].
+
+    ``topk_idx`` / ``topk_w`` (optional, int32 / float32 [T, k]) receive the
+    routing; ``workspace`` (optional uint8 tensor) is reused when large enough.
+    """
+    lib = load_library()
+    T, d = x.shape
+    E, N, d2 = expert_w.shape
+    if d2 != d:
+        raise ValueError("expert_w's last dim must equal x's width")
+    if n_kv_heads is None:
+        n_kv_heads = N // head_dim
+    if n_kv_heads * head_dim != N:
+        raise ValueError("n_kv_heads * head_dim must equal the expert width")
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(router_w, "router_w", torch.bfloat16, (E, d), dev)
+    if router_b is not None:
+        _check(router_b, "router_b", torch.float32, (E,), dev)
+    _check(expert_w, "expert_w", torch.bfloat16, (E, N, d), dev)
+    if out is None:
+        out = torch.empty(T, n_kv_heads, head_dim, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, n_kv_heads, head_dim), dev)
+    if topk_idx is not None:
+        _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    if topk_w is not None:
+        _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    nbytes = workspace_bytes(T, d, E, k, n_kv_heads, head_dim)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = lib.mova_value_forward(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_w),
+                                T, d, E, k, float(scale), n_kv_heads, head_dim, _ptr(out),
+                                _ptr(topk_idx), _ptr(topk_w), _ptr(workspace),
+                                workspace.numel(), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_value_forward")
+    return out
+
+
+def timing_enable(capacity: int, stages=STAGES) -> None:
+    """Record HIP events around the named stages for up to ``capacity`` calls."""
+    mask = 0
+    for s in stages:
+        mask |= 1 << STAGES.index(s)
+    rc = load_library().mova_timing_enable(int(capacity), mask)
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_timing_enable")
+
+
+def timing_read() -> List[Tuple[float, int]]:
+    """[(total_ms, launches)] per stage, in the order of ``STAGES``."""
+    n = len(STAGES)
+    tot = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    rc = load_library().mova_timing_read(n, tot, cnt)
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_timing_read")
+    return [(tot[i], cnt[i]) for i in range(n)]

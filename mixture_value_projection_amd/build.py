@@ -1,0 +1,65 @@
+"""Build ``libmova.so`` (the C-ABI library) in-tree with hipcc for gfx950.
+
+Usage: ``python -m mixture_value_projection_amd.build`` or ``build_library()``.
+Each ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in parallel),
+then linked into ``mixture_value_projection_amd/lib/libmova.so``.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "lib")
+LIBPATH = os.path.join(LIBDIR, "libmova.so")
+BUILDDIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Packed-fp32 instructions are disabled for every device compile.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+          "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
+
+
+def sources():
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILDDIR, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    noise = "is not a recognized feature for this target"
+    warn = "\n".join(l for l in r.stderr.splitlines() if noise not in l and l.strip())
+    if warn:
+        print(warn, file=sys.stderr)
+    return obj
+
+
+def build_library(verbose: bool = True) -> str:
+    """Compile every kernel source and link libmova.so; returns its path."""
+    os.makedirs(BUILDDIR, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIBPATH + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIBPATH)
+    if verbose:
+        print(f"built {LIBPATH}")
+    return LIBPATH
+
+
+if __name__ == "__main__":
+    build_library()

@@ -1,0 +1,56 @@
+// k-way combine: out[t, n] = sum_{i<k} partial[t * k + i, n], summed in slot
+// order i = 0 .. k-1 in fp32 and rounded once to bf16 (nearest even).  The
+// [T, N] result is the [T, n_kv_heads, head_dim] value tensor with column
+// n = h * head_dim + j (page "MoVA: routing the value vectors ...", section
+// "Where the routing happens": the mixture is summed per token and viewed as
+// heads of 128).
+#include <algorithm>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mova {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
+                                                      bf16_t* __restrict__ out, int T, int N, int k) {
+  const int vec_per_row = N / 8;
+  const long long total = (long long)T * vec_per_row;
+  for (long long v = blockIdx.x * 256ll + threadIdx.x; v < total; v += (long long)gridDim.x * 256) {
+    const long long t = v / vec_per_row;
+    const int c = (int)(v % vec_per_row) * 8;
+    const float* src = partial + (size_t)t * k * N + c;
+    float s[8];
+    {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = lo[i];
+        s[i + 4] = hi[i];
+      }
+    }
+    for (int j = 1; j < k; ++j) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src + (size_t)j * N);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + (size_t)j * N + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] += lo[i];
+        s[i + 4] += hi[i];
+      }
+    }
+    u32x4 packed;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      packed[i] = (uint32_t)f32_to_bf16_bits(s[2 * i]) | ((uint32_t)f32_to_bf16_bits(s[2 * i + 1]) << 16);
+    store16(out + (size_t)t * N + c, packed);
+  }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  const long long total = (long long)a.T * (a.N / 8);
+  const long long blocks = std::min<long long>((total + 255) / 256, 256ll * 16);
+  combine_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k);
+  return hipGetLastError();
+}
+
+}  // namespace mova

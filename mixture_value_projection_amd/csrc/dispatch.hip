@@ -1,0 +1,130 @@
+// Dispatch: group the (token, slot) pairs by expert for the grouped GEMM.
+//
+// The reference implementation walks the touched experts one by one in a
+// Python loop (page "MoVA: routing the value vectors ...", section "So what
+// does it cost?").  Here the router already left a per-chunk, per-expert
+// count (chunk = one router workgroup's tokens).  Two kernels finish the job
+// without atomics on global memory:
+//
+//   scan:    per expert, exclusive prefix of the counts over chunks (in
+//            place), expert offsets, and the first M-tile of each expert;
+//   scatter: each chunk re-reads its routing and writes every pair id
+//            (t * k + slot) at expert_off[e] + chunk_off[c][e] + rank, where
+//            rank counts earlier pairs of the same expert in the chunk.
+//
+// The result is stable: within an expert, pairs appear in increasing pair id,
+// so the GEMM's row order -- and hence every output bit -- is independent of
+// scheduling.
+#include "common.h"
+#include "kernels.h"
+
+namespace mova {
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanSub = kScanThreads / kMaxExperts;  // threads per expert
+
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
+    int32_t* __restrict__ counts, int C, int E, int block_m,
+    int32_t* __restrict__ expert_off, int32_t* __restrict__ tile_base) {
+  __shared__ int part[kMaxExperts][kScanSub];
+  __shared__ int total[kMaxExperts];
+  const int e = threadIdx.x / kScanSub;
+  const int sub = threadIdx.x % kScanSub;
+  const int per = ceil_div(C, kScanSub);
+  const int c0 = min(C, sub * per), c1 = min(C, c0 + per);
+
+  int s = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c) s += counts[(size_t)c * E + e];
+  part[e][sub] = s;
+  __syncthreads();
+  if (sub == 0) {
+    int run = 0;
+    for (int i = 0; i < kScanSub; ++i) {
+      const int v = part[e][i];
+      part[e][i] = run;
+      run += v;
+    }
+    total[e] = e < E ? run : 0;
+  }
+  __syncthreads();
+  if (e < E) {
+    int run = part[e][sub];
+    for (int c = c0; c < c1; ++c) {
+      const int v = counts[(size_t)c * E + e];
+      counts[(size_t)c * E + e] = run;
+      run += v;
+    }
+  }
+  if (threadIdx.x == 0) {
+    int off = 0, tiles = 0;
+    for (int i = 0; i < E; ++i) {
+      expert_off[i] = off;
+      tile_base[i] = tiles;
+      off += total[i];
+      tiles += ceil_div(total[i], block_m);
+    }
+    expert_off[E] = off;
+    tile_base[E] = tiles;
+  }
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_off,
+    const int32_t* __restrict__ expert_off, int32_t* __restrict__ perm,
+    int T, int E, int k, int chunk_tokens) {
+  __shared__ int running[kMaxExperts];
+  __shared__ int wave_cnt[4][kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c = blockIdx.x;
+  const int p0 = c * chunk_tokens * k;
+  const int npairs = min(T * k, p0 + chunk_tokens * k) - p0;
+
+  if (threadIdx.x < kMaxExperts) running[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < 4 * kMaxExperts; i += 256) (&wave_cnt[0][0])[i] = 0;
+  __syncthreads();
+
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = 0; base < npairs; base += 256) {
+    const int p = base + threadIdx.x;
+    const bool valid = p < npairs;
+    const int e = valid ? idx[p0 + p] : 0;
+    // Lanes of this wave holding the same expert (6 ballots over the id bits).
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t on = __ballot(bit);
+      peers &= bit ? on : ~on;
+    }
+    const int rank_in_wave = __popcll(peers & lt_mask);
+    if (valid && rank_in_wave == 0) wave_cnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (valid) {
+      int rank = running[e] + rank_in_wave;
+      for (int w = 0; w < wave; ++w) rank += wave_cnt[w][e];
+      perm[expert_off[e] + chunk_off[(size_t)c * E + e] + rank] = p0 + p;
+    }
+    __syncthreads();
+    if (threadIdx.x < kMaxExperts) {
+      const int x = threadIdx.x;
+      running[x] += wave_cnt[0][x] + wave_cnt[1][x] + wave_cnt[2][x] + wave_cnt[3][x];
+      wave_cnt[0][x] = wave_cnt[1][x] = wave_cnt[2][x] = wave_cnt[3][x] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
+  const int C = ceil_div(a.T, a.chunk_tokens);
+  dispatch_scan_kernel<<<1, kScanThreads, 0, stream>>>(a.chunk_counts, C, a.E, a.block_m,
+                                                       a.expert_off, a.tile_base);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  dispatch_scatter_kernel<<<C, 256, 0, stream>>>(a.idx, a.chunk_counts, a.expert_off, a.perm,
+                                                 a.T, a.E, a.k, a.chunk_tokens);
+  return hipGetLastError();
+}
+
+}  // namespace mova

@@ -1,0 +1,69 @@
+// Internal launch interface between the C ABI (mova_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mova {
+
+struct RouterArgs {
+  const __bf16* x;
+  const __bf16* wr;
+  const float* bias;  // may be null
+  int T, d, E, k;
+  float scale;
+  int32_t* idx;           // [T, k]
+  float* w;               // [T, k]
+  int32_t* chunk_counts;  // [blocks, E] or null
+};
+
+// Router blocks cover 16 tokens ("narrow", small T) or 64 ("wide").
+int router_tokens_per_block(bool wide);
+hipError_t launch_router(const RouterArgs& a, bool wide, hipStream_t stream);
+
+struct DispatchArgs {
+  const int32_t* idx;     // [T, k] routing
+  int32_t* chunk_counts;  // [C, E] in: per-chunk counts; out: per-chunk offsets
+  int32_t* expert_off;    // [E + 1] out: first sorted pair of each expert
+  int32_t* tile_base;     // [E + 1] out: first M-tile of each expert
+  int32_t* perm;          // [T * k] out: pair ids (t * k + slot) grouped by expert, stable
+  int T, E, k;
+  int chunk_tokens;  // tokens per chunk (router block)
+  int block_m;       // M-tile height of the grouped GEMM
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
+
+struct GemmArgs {
+  const __bf16* x;         // [T, d]
+  const __bf16* W;         // [E, N, d]
+  const int32_t* perm;     // [T * k]
+  const float* topk_w;     // [T * k]
+  const int32_t* expert_off;
+  const int32_t* tile_base;
+  float* partial;          // [T * k, N]
+  int T, d, N, E, k;
+};
+int gemm_block_m();
+// Upper bound on M-tiles for any routing of T tokens.
+int gemm_max_mtiles(int T, int k, int E);
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const __bf16* x;
+  const __bf16* W;
+  const int32_t* idx;   // [T, k]
+  const float* topk_w;  // [T, k]
+  float* partial;       // [T * k, N]
+  int T, d, N, E, k;
+};
+constexpr int kDecodeMaxPairs = 4096;
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+  const float* partial;  // [T * k, N]
+  __bf16* out;           // [T, N]
+  int T, N, k;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace mova

@@ -1,0 +1,266 @@
+// C ABI of the MoVA routed value projection: argument checks, workspace
+// layout, path choice and launches.  Declarations and contracts: include/mova.h.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/mova.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using namespace mova;
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int kMaxT = 1 << 24;
+// Token counts up to this take the weight-streaming decode path.
+constexpr int kDecodeMaxT = 64;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape check shared by every entry point; returns MOVA_OK or an error.
+int check_shape(int T, int d, int E, int k) {
+  if (T < 0 || d <= 0 || E <= 0 || k <= 0) return MOVA_ERR_INVALID_ARG;
+  if (T > kMaxT) return MOVA_ERR_UNSUPPORTED;
+  if (E > kMaxExperts || k > kMaxTopK || k > E) return MOVA_ERR_UNSUPPORTED;
+  if (d % 64 != 0) return MOVA_ERR_UNSUPPORTED;
+  return MOVA_OK;
+}
+
+int check_heads(int n_kv_heads, int head_dim) {
+  if (n_kv_heads <= 0 || head_dim <= 0) return MOVA_ERR_INVALID_ARG;
+  const long long N = (long long)n_kv_heads * head_dim;
+  if (N % 64 != 0 || N > (1 << 14)) return MOVA_ERR_UNSUPPORTED;
+  return MOVA_OK;
+}
+
+enum class Path { Decode, Grouped };
+
+Path choose_path(int T, int k) {
+  const char* force = getenv("MOVA_PATH");
+  const bool decode_ok = (long long)T * k <= kDecodeMaxPairs;
+  if (force != nullptr) {
+    if (strcmp(force, "decode") == 0 && decode_ok) return Path::Decode;
+    if (strcmp(force, "grouped") == 0) return Path::Grouped;
+  }
+  return (T <= kDecodeMaxT && decode_ok) ? Path::Decode : Path::Grouped;
+}
+
+// Workspace layout (every region 256-byte aligned):
+//   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] i32 |
+//   tile_base [E+1] i32 | perm [T*k] i32 | partial [T*k*N] f32
+struct Layout {
+  size_t idx, w, chunk, eoff, tbase, perm, partial, total;
+};
+
+Layout layout(int T, int E, int k, int N) {
+  const size_t pairs = (size_t)T * k;
+  const size_t C = (size_t)ceil_div(T, router_tokens_per_block(true));
+  Layout L;
+  size_t o = 0;
+  L.idx = o;     o += align256(pairs * 4);
+  L.w = o;       o += align256(pairs * 4);
+  L.chunk = o;   o += align256(C * E * 4);
+  L.eoff = o;    o += align256((size_t)(E + 1) * 4);
+  L.tbase = o;   o += align256((size_t)(E + 1) * 4);
+  L.perm = o;    o += align256(pairs * 4);
+  L.partial = o; o += align256(pairs * N * 4);
+  L.total = o;
+  return L;
+}
+
+// ---- stage timing -------------------------------------------------------
+constexpr int kStages = 4;
+struct Timing {
+  std::mutex mu;
+  int capacity = 0;
+  unsigned mask = 0;
+  std::vector<hipEvent_t> ev[kStages];  // pairs: start at 2i, stop at 2i+1
+  int used[kStages] = {0, 0, 0, 0};
+} g_timing;
+
+struct StageScope {
+  int stage;
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  StageScope(int st, hipStream_t stream) : stage(st), s(stream) {
+    if (g_timing.capacity <= 0 || !(g_timing.mask & (1u << st))) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    const int u = g_timing.used[stage];
+    if (u >= g_timing.capacity) return;
+    (void)hipEventRecord(g_timing.ev[stage][2 * u], s);
+    stop = g_timing.ev[stage][2 * u + 1];
+    g_timing.used[stage] = u + 1;
+  }
+  ~StageScope() {
+    if (stop != nullptr) (void)hipEventRecord(stop, s);
+  }
+};
+
+void timing_free() {
+  for (int s = 0; s < kStages; ++s) {
+    for (hipEvent_t e : g_timing.ev[s])
+      if (e != nullptr) (void)hipEventDestroy(e);
+    g_timing.ev[s].clear();
+    g_timing.used[s] = 0;
+  }
+  g_timing.capacity = 0;
+  g_timing.mask = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mova_version(void) { return kVersion; }
+
+const char* mova_status_str(int status) {
+  switch (status) {
+    case MOVA_OK: return "MOVA_OK";
+    case MOVA_ERR_INVALID_ARG: return "MOVA_ERR_INVALID_ARG: null/misaligned pointer or negative size";
+    case MOVA_ERR_UNSUPPORTED: return "MOVA_ERR_UNSUPPORTED: shape outside the supported domain";
+    case MOVA_ERR_WORKSPACE: return "MOVA_ERR_WORKSPACE: workspace missing or too small";
+    case MOVA_ERR_HIP: return "MOVA_ERR_HIP: a HIP launch or runtime call failed";
+    default: return "MOVA: unknown status";
+  }
+}
+
+size_t mova_workspace_bytes(int T, int d, int E, int k, int n_kv_heads, int head_dim) {
+  if (check_shape(T, d, E, k) != MOVA_OK || check_heads(n_kv_heads, head_dim) != MOVA_OK)
+    return (size_t)-1;
+  if (T == 0) return 0;
+  return layout(T, E, k, n_kv_heads * head_dim).total;
+}
+
+int mova_route(const void* x, const void* router_w, const float* router_b, int T, int d, int E,
+               int k, float scale, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  int rc = check_shape(T, d, E, k);
+  if (rc != MOVA_OK) return rc;
+  if (!isfinite(scale)) return MOVA_ERR_UNSUPPORTED;
+  if (T == 0) return MOVA_OK;
+  if (x == nullptr || router_w == nullptr || topk_idx == nullptr || topk_w == nullptr)
+    return MOVA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(router_b) || !aligned16(topk_idx) ||
+      !aligned16(topk_w))
+    return MOVA_ERR_INVALID_ARG;
+  RouterArgs ra{(const __bf16*)x, (const __bf16*)router_w, router_b, T, d, E, k, scale,
+                topk_idx, topk_w, nullptr};
+  const bool wide = T > kDecodeMaxT;
+  return launch_router(ra, wide, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+}
+
+int mova_value_forward(const void* x, const void* router_w, const float* router_b,
+                       const void* expert_w, int T, int d, int E, int k, float scale,
+                       int n_kv_heads, int head_dim, void* out, int32_t* topk_idx_out,
+                       float* topk_w_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  int rc = check_shape(T, d, E, k);
+  if (rc != MOVA_OK) return rc;
+  rc = check_heads(n_kv_heads, head_dim);
+  if (rc != MOVA_OK) return rc;
+  if (!isfinite(scale)) return MOVA_ERR_UNSUPPORTED;
+  if (T == 0) return MOVA_OK;
+  if (x == nullptr || router_w == nullptr || expert_w == nullptr || out == nullptr)
+    return MOVA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(router_b) || !aligned16(expert_w) ||
+      !aligned16(out) || !aligned16(topk_idx_out) || !aligned16(topk_w_out))
+    return MOVA_ERR_INVALID_ARG;
+  const int N = n_kv_heads * head_dim;
+  const Layout L = layout(T, E, k, N);
+  if (workspace == nullptr || workspace_bytes < L.total) return MOVA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOVA_ERR_INVALID_ARG;
+
+  char* ws = (char*)workspace;
+  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(ws + L.idx);
+  float* w = topk_w_out ? topk_w_out : (float*)(ws + L.w);
+  int32_t* chunk = (int32_t*)(ws + L.chunk);
+  int32_t* eoff = (int32_t*)(ws + L.eoff);
+  int32_t* tbase = (int32_t*)(ws + L.tbase);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  float* partial = (float*)(ws + L.partial);
+  const __bf16* xb = (const __bf16*)x;
+  const __bf16* wb = (const __bf16*)expert_w;
+
+  const Path path = choose_path(T, k);
+  const bool wide = path == Path::Grouped;
+  hipError_t err;
+  {
+    StageScope sc(0, stream);
+    RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w,
+                  wide ? chunk : nullptr};
+    err = launch_router(ra, wide, stream);
+  }
+  if (err != hipSuccess) return MOVA_ERR_HIP;
+
+  if (path == Path::Decode) {
+    StageScope sc(2, stream);
+    DecodeArgs da{xb, wb, idx, w, partial, T, d, N, E, k};
+    err = launch_decode(da, stream);
+  } else {
+    {
+      StageScope sc(1, stream);
+      DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, router_tokens_per_block(true),
+                      gemm_block_m()};
+      err = launch_dispatch(dp, stream);
+    }
+    if (err != hipSuccess) return MOVA_ERR_HIP;
+    StageScope sc(2, stream);
+    GemmArgs ga{xb, wb, perm, w, eoff, tbase, partial, T, d, N, E, k};
+    err = launch_grouped_gemm(ga, stream);
+  }
+  if (err != hipSuccess) return MOVA_ERR_HIP;
+  {
+    StageScope sc(3, stream);
+    CombineArgs ca{partial, (__bf16*)out, T, N, k};
+    err = launch_combine(ca, stream);
+  }
+  return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+}
+
+int mova_timing_enable(int capacity, unsigned stage_mask) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  timing_free();
+  stage_mask &= (1u << kStages) - 1;
+  if (capacity <= 0 || stage_mask == 0) return MOVA_OK;
+  for (int s = 0; s < kStages; ++s) {
+    if (!(stage_mask & (1u << s))) continue;
+    g_timing.ev[s].resize(2 * (size_t)capacity, nullptr);
+    for (auto& e : g_timing.ev[s]) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        e = nullptr;
+        timing_free();
+        return MOVA_ERR_HIP;
+      }
+    }
+  }
+  g_timing.capacity = capacity;
+  g_timing.mask = stage_mask;
+  return MOVA_OK;
+}
+
+int mova_timing_read(int n, double* total_ms, int* count) {
+  if (n < 0 || (n > 0 && (total_ms == nullptr || count == nullptr))) return MOVA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (int s = 0; s < n; ++s) {
+    total_ms[s] = 0.0;
+    count[s] = 0;
+    if (s >= kStages) continue;
+    for (int u = 0; u < g_timing.used[s]; ++u) {
+      hipEvent_t a = g_timing.ev[s][2 * u], b = g_timing.ev[s][2 * u + 1];
+      if (hipEventSynchronize(b) != hipSuccess) return MOVA_ERR_HIP;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, a, b) != hipSuccess) return MOVA_ERR_HIP;
+      total_ms[s] += ms;
+    }
+    count[s] = g_timing.used[s];
+  }
+  return MOVA_OK;
+}
+
+}  // extern "C"

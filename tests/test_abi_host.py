@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, and rejects bad arguments before touching the GPU.
+
+Every call here returns from the library's argument checks (or is T == 0),
+so no kernel is launched and no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_value_projection_amd import binding
+from mixture_value_projection_amd.build import LIBPATH
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mova.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+FAKE = 1 << 20  # an aligned non-null address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIBPATH):
+        pytest.fail(f"{LIBPATH} not built (run __graft_entry__.build())")
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(mova_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("mova_route", "mova_value_forward", "mova_workspace_bytes", "mova_status_str",
+              "mova_version", "mova_timing_enable", "mova_timing_read"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in mova.h but not exported"
+
+
+def test_status_strings(lib):
+    for rc, tag in [(OK, "MOVA_OK"), (INVALID, "INVALID_ARG"), (UNSUPPORTED, "UNSUPPORTED"),
+                    (WORKSPACE, "WORKSPACE"), (HIPERR, "HIP")]:
+        assert tag in binding.status_str(rc)
+    assert "unknown" in binding.status_str(12345)
+    assert binding.version() >= 100
+
+
+def test_workspace_bytes(lib):
+    assert binding.workspace_bytes(0, 2560, 64, 4, 8, 128) == 0
+    prev = 0
+    for T in (1, 16, 64, 65, 4096, 32768):
+        n = binding.workspace_bytes(T, 2560, 64, 4, 8, 128)
+        assert n > prev and n % 256 == 0
+        assert n >= T * 4 * 1024 * 4   # fp32 slot partials
+        prev = n
+    bad = ctypes.c_size_t(-1).value
+    assert lib.mova_workspace_bytes(16, 2560, 65, 4, 8, 128) == bad     # E > 64
+    assert lib.mova_workspace_bytes(16, 2560, 64, 9, 8, 128) == bad     # k > 8
+    assert lib.mova_workspace_bytes(16, 2500, 64, 4, 8, 128) == bad     # d % 64
+    assert lib.mova_workspace_bytes(16, 2560, 64, 4, 3, 20) == bad      # N % 64
+    assert lib.mova_workspace_bytes(-1, 2560, 64, 4, 8, 128) == bad
+
+
+def fwd(lib, **kw):
+    a = dict(x=FAKE, rw=FAKE, rb=None, ew=FAKE, T=16, d=256, E=8, k=2, scale=2.5, H=2, D=32,
+             out=FAKE, idx=None, w=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mova_value_forward(a["x"], a["rw"], a["rb"], a["ew"], a["T"], a["d"], a["E"], a["k"],
+                                  a["scale"], a["H"], a["D"], a["out"], a["idx"], a["w"], a["ws"],
+                                  a["wsb"], a["stream"])
+
+
+def rte(lib, **kw):
+    a = dict(x=FAKE, rw=FAKE, rb=None, T=16, d=256, E=8, k=2, scale=2.5, idx=FAKE, w=FAKE,
+             stream=None)
+    a.update(kw)
+    return lib.mova_route(a["x"], a["rw"], a["rb"], a["T"], a["d"], a["E"], a["k"], a["scale"],
+                          a["idx"], a["w"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), INVALID), (dict(d=0), INVALID), (dict(E=0), INVALID), (dict(k=0), INVALID),
+    (dict(E=65), UNSUPPORTED), (dict(k=9, E=16), UNSUPPORTED), (dict(k=3, E=2), UNSUPPORTED),
+    (dict(d=100), UNSUPPORTED), (dict(H=3, D=20), UNSUPPORTED), (dict(H=0), INVALID),
+    (dict(scale=float("nan")), UNSUPPORTED), (dict(scale=float("inf")), UNSUPPORTED),
+    (dict(T=(1 << 24) + 1), UNSUPPORTED), (dict(H=129, D=128), UNSUPPORTED),
+    (dict(x=None), INVALID), (dict(rw=None), INVALID), (dict(ew=None), INVALID),
+    (dict(out=None), INVALID), (dict(x=FAKE + 2), INVALID), (dict(ew=FAKE + 8), INVALID),
+    (dict(rb=FAKE + 4), INVALID), (dict(idx=FAKE + 4), INVALID), (dict(out=FAKE + 2), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=FAKE + 16), INVALID),
+])
+def test_value_forward_rejects(lib, kw, rc):
+    assert fwd(lib, **kw) == rc
+
+
+def test_value_forward_empty_is_noop(lib):
+    # T == 0: nothing is enqueued, even with null buffers.
+    assert fwd(lib, T=0, x=None, out=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-5), INVALID), (dict(E=70), UNSUPPORTED), (dict(k=5, E=4), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(scale=float("nan")), UNSUPPORTED),
+    (dict(x=None), INVALID), (dict(idx=None), INVALID), (dict(w=None), INVALID),
+    (dict(w=FAKE + 4), INVALID),
+])
+def test_route_rejects(lib, kw, rc):
+    assert rte(lib, **kw) == rc
+
+
+def test_route_empty_is_noop(lib):
+    assert rte(lib, T=0, x=None, idx=None, w=None) == OK
+
+
+def test_timing_read_without_records(lib):
+    tot = (ctypes.c_double * 4)()
+    cnt = (ctypes.c_int * 4)()
+    assert lib.mova_timing_read(4, tot, cnt) == OK
+    assert list(cnt) == [0, 0, 0, 0]
+    assert lib.mova_timing_read(-1, tot, cnt) == INVALID
+
+
+def test_binding_rejects_wrong_dtype_on_cpu():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        binding.route(x, torch.zeros(8, 64, dtype=torch.bfloat16), None, 2)
