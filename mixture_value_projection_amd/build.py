@@ -20,8 +20,16 @@ BUILDDIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed-fp32 instructions are disabled for every device compile.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Device code generation flags:
+# * packed-fp32 instructions are disabled for every device compile;
+# * MFMA accumulators are kept in (and updated in place in) ordinary VGPRs.
+#   With the default AGPR heuristics, loops whose accumulators are updated
+#   under data-dependent branches were compiled into AGPR<->VGPR copies and
+#   rotations at the loop head, and the copied values were read before the
+#   MFMA that produced them had finished (wrong, run-to-run varying results).
+#   tests/test_codegen.py checks that no AGPR copy instruction is emitted.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 
@@ -41,6 +49,15 @@ def _compile(src: str) -> str:
     if warn:
         print(warn, file=sys.stderr)
     return obj
+
+
+def device_asm(src: str) -> str:
+    """gfx950 assembly of one source file, compiled with the library's flags."""
+    cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "--cuda-device-only", "-S", src, "-o", "-"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    return r.stdout
 
 
 def build_library(verbose: bool = True) -> str:

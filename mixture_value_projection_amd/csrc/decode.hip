@@ -22,6 +22,70 @@ constexpr int kSlice = 64;   // columns per workgroup
 constexpr int kGroups = 4;   // 16-token MFMA groups per pass (64 tokens)
 constexpr int kUnroll = 8;   // k steps whose weight loads are in flight together
 
+// One pass over the slice's weights for NG groups of 16 tokens starting at
+// plist[p0].  NG is a template argument so that every MFMA in the k loop runs
+// unconditionally: accumulators updated under data-dependent branches were
+// compiled into AGPR<->VGPR copies at the loop head that read MFMA results too
+// early.
+template <int NG>
+__device__ __forceinline__ void decode_pass(const bf16_t* __restrict__ x, const bf16_t* wrow,
+                                            const int* plist, int p0, int ce,
+                                            const float* __restrict__ topk_w,
+                                            float* __restrict__ partial, int d, int N, int k,
+                                            int n, int q, int r16) {
+  const bf16_t* xrow[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int r = min(p0 + g * 16 + r16, ce - 1);
+    xrow[g] = x + (size_t)(plist[r] / k) * d + q * 8;
+  }
+  f32x4 acc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int steps = d / 32;  // even, since d % 64 == 0
+  int s = 0;
+  for (; s + kUnroll <= steps; s += kUnroll) {
+    Frag16 b[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) b[u].u = load16(wrow + (s + u) * 32);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        Frag16 a;
+        a.u = load16(xrow[g] + (s + u) * 32);
+        acc[g] = mfma16x16x32(a.h, b[u].h, acc[g]);
+      }
+    }
+  }
+  for (; s < steps; s += 2) {
+    Frag16 b0, b1;
+    b0.u = load16(wrow + s * 32);
+    b1.u = load16(wrow + (s + 1) * 32);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      Frag16 a0, a1;
+      a0.u = load16(xrow[g] + s * 32);
+      a1.u = load16(xrow[g] + (s + 1) * 32);
+      acc[g] = mfma16x16x32(a0.h, b0.h, acc[g]);
+      acc[g] = mfma16x16x32(a1.h, b1.h, acc[g]);
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = p0 + g * 16 + q * 4 + v;
+      if (r < ce) {
+        const int pair = plist[r];
+        partial[(size_t)pair * N + n] = topk_w[pair] * siluf(acc[g][v]);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
@@ -55,63 +119,16 @@ __global__ __launch_bounds__(256) void decode_kernel(
 
   const int n = n0 + wave * 16 + r16;
   const bf16_t* wrow = W + ((size_t)e * N + n) * d + q * 8;
-  const int steps = d / 32;
-
   for (int p0 = 0; p0 < ce; p0 += kGroups * 16) {
     const int ng = min(kGroups, ceil_div(ce - p0, 16));
-    const bf16_t* xrow[kGroups];
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      const int r = min(p0 + g * 16 + r16, ce - 1);
-      xrow[g] = x + (size_t)(plist[r] / k) * d + q * 8;
-    }
-    f32x4 acc[kGroups];
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    int s = 0;
-    for (; s + kUnroll <= steps; s += kUnroll) {
-      Frag16 b[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) b[u].u = load16(wrow + (s + u) * 32);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-          if (g < ng) {
-            Frag16 a;
-            a.u = load16(xrow[g] + (s + u) * 32);
-            acc[g] = mfma16x16x32(a.h, b[u].h, acc[g]);
-          }
-        }
-      }
-    }
-    for (; s < steps; ++s) {
-      Frag16 b;
-      b.u = load16(wrow + s * 32);
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        if (g < ng) {
-          Frag16 a;
-          a.u = load16(xrow[g] + s * 32);
-          acc[g] = mfma16x16x32(a.h, b.h, acc[g]);
-        }
-      }
-    }
-
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      if (g < ng) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int r = p0 + g * 16 + q * 4 + v;
-          if (r < ce) {
-            const int pair = plist[r];
-            partial[(size_t)pair * N + n] = topk_w[pair] * siluf(acc[g][v]);
-          }
-        }
-      }
-    }
+    if (ng == 1)
+      decode_pass<1>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
+    else if (ng == 2)
+      decode_pass<2>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
+    else if (ng == 3)
+      decode_pass<3>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
+    else
+      decode_pass<4>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
   }
 }
 

@@ -6,85 +6,72 @@
 // notice", section "Where the routing happens" (weight-only router linear map,
 // sigmoid scoring, top-4, scaling factor 2.5).
 //
-// One workgroup = 4 waves handles TM = 16 * WT tokens.  The d-long dot
-// products are split into four residue classes of 32-wide k steps (step mod
-// 4), spread over WK = 4 / WT waves; the four partial logits meet in LDS and
-// are added in residue order, so every block shape yields the same bits.
-// Top-k then runs with one lane per expert (E <= 64).
-// Optionally each workgroup writes how many of its (token, slot) pairs chose
-// each expert -- the per-chunk histogram the dispatch step scans.
+// One workgroup = 4 waves handles TM = 16 * TG tokens.  The d-long dot
+// products are split into four residue classes of 32-wide k steps
+// (step mod 4); wave w owns class w for all of the block's tokens and all 64
+// expert columns (TG x 4 MFMA tiles, accumulated in place).  The four partial
+// logits meet in LDS and are added in class order, so a token's logits are
+// the same bits whichever block shape (or call) processed it.  Top-k then
+// runs with one lane per expert (E <= 64).  Optionally each workgroup writes
+// how many of its (token, slot) pairs chose each expert -- the per-chunk
+// histogram the dispatch step scans.
 #include "common.h"
 #include "kernels.h"
 
 namespace mova {
 
-template <int WT>
+template <int TG>
 __global__ __launch_bounds__(256) void router_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int E, int k, float scale,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts) {
-  constexpr int WK = 4 / WT;   // waves sharing one token group's k steps
-  constexpr int RPW = 4 / WK;  // k-step residue classes (mod 4) per wave
-  constexpr int TM = 16 * WT;
+  constexpr int TM = 16 * TG;
   __shared__ float part[4][TM][kMaxExperts];
   __shared__ int hist[kMaxExperts];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wt = wave % WT;
-  const int wk = wave / WT;
+  const int wave = threadIdx.x >> 6;  // k-step residue class
   const int q = lane >> 4;
   const int r16 = lane & 15;
   const int tile_t0 = blockIdx.x * TM;
 
   if (threadIdx.x < kMaxExperts) hist[threadIdx.x] = 0;
 
-  // A operand: token row (clamped into range; rows past T are never written).
-  const int trow = min(tile_t0 + wt * 16 + r16, T - 1);
-  const bf16_t* xrow = x + (size_t)trow * d + q * 8;
+  // A operand: token rows (clamped into range; rows past T are never written).
+  const bf16_t* xrow[TG];
+#pragma unroll
+  for (int g = 0; g < TG; ++g)
+    xrow[g] = x + (size_t)min(tile_t0 + g * 16 + r16, T - 1) * d + q * 8;
   // B operand: expert rows (clamped; lanes for experts >= E are masked in top-k).
   const bf16_t* wrow[4];
 #pragma unroll
   for (int eb = 0; eb < 4; ++eb) wrow[eb] = wr + (size_t)min(eb * 16 + r16, E - 1) * d + q * 8;
-  const int EB = ceil_div(E, 16);
 
-  // acc[rr] sums the 32-wide k steps s with s % 4 == wk * RPW + rr.  Both
-  // block shapes therefore add the same products in the same order, and the
-  // four residue sums are added in residue order below: a token's logits do
-  // not depend on which block shape (or call) processed it.
-  f32x4 acc[RPW][4];
+  f32x4 acc[TG][4];
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr)
+  for (int g = 0; g < TG; ++g)
 #pragma unroll
-    for (int eb = 0; eb < 4; ++eb) acc[rr][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int eb = 0; eb < 4; ++eb) acc[g][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int steps = d / 32;
-  for (int s4 = 0; s4 < steps; s4 += 4) {
+  for (int s = wave; s < steps; s += 4) {
+    Frag16 a[TG], b[4];
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) {
-      const int s = s4 + wk * RPW + rr;
-      if (s < steps) {
-        Frag16 a;
-        a.u = load16(xrow + s * 32);
+    for (int g = 0; g < TG; ++g) a[g].u = load16(xrow[g] + s * 32);
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb) {
-          if (eb < EB) {
-            Frag16 b;
-            b.u = load16(wrow[eb] + s * 32);
-            acc[rr][eb] = mfma16x16x32(a.h, b.h, acc[rr][eb]);
-          }
-        }
-      }
-    }
+    for (int eb = 0; eb < 4; ++eb) b[eb].u = load16(wrow[eb] + s * 32);
+#pragma unroll
+    for (int g = 0; g < TG; ++g)
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) acc[g][eb] = mfma16x16x32(a[g].h, b[eb].h, acc[g][eb]);
   }
 
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr)
+  for (int g = 0; g < TG; ++g)
 #pragma unroll
     for (int eb = 0; eb < 4; ++eb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        part[wk * RPW + rr][wt * 16 + q * 4 + i][eb * 16 + r16] = acc[rr][eb][i];
+      for (int i = 0; i < 4; ++i) part[wave][g * 16 + q * 4 + i][eb * 16 + r16] = acc[g][eb][i];
   __syncthreads();
 
   // Top-k: wave `wave` takes tile rows wave, wave + 4, ...; lane = expert.
