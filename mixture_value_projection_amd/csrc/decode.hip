@@ -11,96 +11,53 @@
 // pair order.
 //
 // Each wave owns 16 of the slice's columns; its 64 lanes read 16 rows x 64 B
-// per 32-wide k step (whole 128 B lines over two steps).  The fused epilogue
-// writes w * SiLU(z) to the pair's partial row, like the grouped GEMM.
+// per 32-wide k step.  The k loop runs in batches of kUnroll steps: a batch's
+// weight loads are issued first, then the token rows of the next batch are
+// copied into LDS (double-buffered, 16-byte chunks XOR-swizzled by row), then
+// the batch's MFMAs read their token operand from LDS.  Tokens are handled 16
+// at a time (one MFMA row group); an expert with more than 16 tokens takes
+// several passes over its weights.  The epilogue writes w * SiLU(z) to the
+// pair's partial row, like the grouped GEMM.
+//
+// Fused combine: the E workgroups of one column slice each bump that slice's
+// arrival counter (agent-scope release after their partial rows are written);
+// the last to arrive acquires and sums the slice's k partials per token in slot
+// order into the bf16 output -- the same fixed-order sum as the combine kernel
+// of the grouped path, so both paths give identical bits.  The counters are
+// zeroed by the router earlier in the same call.
 #include "common.h"
 #include "kernels.h"
 
 namespace mova {
 
-constexpr int kSlice = 64;   // columns per workgroup
-constexpr int kGroups = 4;   // 16-token MFMA groups per pass (64 tokens)
-constexpr int kUnroll = 8;   // k steps whose weight loads are in flight together
+constexpr int kSlice = 64;    // columns per workgroup
+constexpr int kUnroll = 8;    // k steps per batch
+constexpr int kRowBytes = kUnroll * 64;       // one token's k range per batch
+constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per staged row
 
-// One pass over the slice's weights for NG groups of 16 tokens starting at
-// plist[p0].  NG is a template argument so that every MFMA in the k loop runs
-// unconditionally: accumulators updated under data-dependent branches were
-// compiled into AGPR<->VGPR copies at the loop head that read MFMA results too
-// early.
-template <int NG>
-__device__ __forceinline__ void decode_pass(const bf16_t* __restrict__ x, const bf16_t* wrow,
-                                            const int* plist, int p0, int ce,
-                                            const float* __restrict__ topk_w,
-                                            float* __restrict__ partial, int d, int N, int k,
-                                            int n, int q, int r16) {
-  const bf16_t* xrow[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int r = min(p0 + g * 16 + r16, ce - 1);
-    xrow[g] = x + (size_t)(plist[r] / k) * d + q * 8;
-  }
-  f32x4 acc[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int steps = d / 32;  // even, since d % 64 == 0
-  int s = 0;
-  for (; s + kUnroll <= steps; s += kUnroll) {
-    Frag16 b[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) b[u].u = load16(wrow + (s + u) * 32);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        Frag16 a;
-        a.u = load16(xrow[g] + (s + u) * 32);
-        acc[g] = mfma16x16x32(a.h, b[u].h, acc[g]);
-      }
-    }
-  }
-  for (; s < steps; s += 2) {
-    Frag16 b0, b1;
-    b0.u = load16(wrow + s * 32);
-    b1.u = load16(wrow + (s + 1) * 32);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      Frag16 a0, a1;
-      a0.u = load16(xrow[g] + s * 32);
-      a1.u = load16(xrow[g] + (s + 1) * 32);
-      acc[g] = mfma16x16x32(a0.h, b0.h, acc[g]);
-      acc[g] = mfma16x16x32(a1.h, b1.h, acc[g]);
-    }
-  }
-
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = p0 + g * 16 + q * 4 + v;
-      if (r < ce) {
-        const int pair = plist[r];
-        partial[(size_t)pair * N + n] = topk_w[pair] * siluf(acc[g][v]);
-      }
-    }
-  }
+__device__ __forceinline__ int xs_off(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
 }
 
 __global__ __launch_bounds__(256) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
     float* __restrict__ partial, int T, int d, int N, int E, int k) {
-  __shared__ int plist[kDecodeMaxPairs];
+  __shared__ int plist[kDecodeMaxT];
+  __shared__ __attribute__((aligned(16))) char xs[2][16 * kRowBytes];
   __shared__ int count;
 
   const int slices = N / kSlice;
   const int e = blockIdx.x / slices;
   const int n0 = (blockIdx.x % slices) * kSlice;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const int npairs = T * k;
 
+  // Pairs routed to this expert, in pair order (a token picks e at most once).
   if (wave == 0) {
     int c = 0;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -115,21 +72,63 @@ __global__ __launch_bounds__(256) void decode_kernel(
   }
   __syncthreads();
   const int ce = count;
-  if (ce == 0) return;
 
   const int n = n0 + wave * 16 + r16;
   const bf16_t* wrow = W + ((size_t)e * N + n) * d + q * 8;
-  for (int p0 = 0; p0 < ce; p0 += kGroups * 16) {
-    const int ng = min(kGroups, ceil_div(ce - p0, 16));
-    if (ng == 1)
-      decode_pass<1>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
-    else if (ng == 2)
-      decode_pass<2>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
-    else if (ng == 3)
-      decode_pass<3>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
-    else
-      decode_pass<4>(x, wrow, plist, p0, ce, topk_w, partial, d, N, k, n, q, r16);
+  const int steps = d / 32;            // even, since d % 64 == 0
+  const int nb = ceil_div(steps, kUnroll);
+  static_assert(16 * kChunks == 2 * 256, "two 16-byte chunks per thread per batch");
+
+  for (int p0 = 0; p0 < ce; p0 += 16) {
+    const bf16_t* src[2];
+    int cp_row[2], cp_ch[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * 256;
+      cp_row[i] = c / kChunks;
+      cp_ch[i] = c % kChunks;
+      const int pair = plist[min(p0 + cp_row[i], ce - 1)];
+      src[i] = x + (size_t)(pair / k) * d;
+    }
+    // Copy batch bt of the 16 token rows into xs[buf].  k offsets past the end
+    // of the row (d not a multiple of the batch) read a clamped address and
+    // store zeros, so those steps contribute nothing.
+    auto stage = [&](int bt, int buf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int kk = bt * kUnroll * 32 + cp_ch[i] * 8;
+        u32x4 v = load16(src[i] + min(kk, d - 8));
+        if (kk >= d) v = u32x4{0u, 0u, 0u, 0u};
+        store16(&xs[buf][xs_off(cp_row[i], cp_ch[i])], v);
+      }
+    };
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    stage(0, 0);
+    __syncthreads();
+    for (int bt = 0; bt < nb; ++bt) {
+      const int buf = bt & 1;
+      Frag16 b[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) b[u].u = load16(wrow + min(bt * kUnroll + u, steps - 1) * 32);
+      if (bt + 1 < nb) stage(bt + 1, buf ^ 1);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        Frag16 a;
+        a.u = load16(&xs[buf][xs_off(r16, u * 4 + q)]);
+        acc = mfma16x16x32(a.h, b[u].h, acc);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = p0 + q * 4 + v;
+      if (r < ce) {
+        const int pair = plist[r];
+        partial[(size_t)pair * N + n] = topk_w[pair] * siluf(acc[v]);
+      }
+    }
   }
+
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

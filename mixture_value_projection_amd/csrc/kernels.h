@@ -20,6 +20,10 @@ struct RouterArgs {
 // Router blocks cover 16 tokens ("narrow", small T) or 64 ("wide").
 int router_tokens_per_block(bool wide);
 hipError_t launch_router(const RouterArgs& a, bool wide, hipStream_t stream);
+// Small-T router: partial logits over many single-wave blocks, then top-k.
+// Same bits as launch_router.  plog: router_small_plog_floats(T) floats.
+int router_small_plog_floats(int T);
+hipError_t launch_router_small(const RouterArgs& a, float* plog, hipStream_t stream);
 
 struct DispatchArgs {
   const int32_t* idx;     // [T, k] routing
@@ -56,7 +60,8 @@ struct DecodeArgs {
   float* partial;       // [T * k, N]
   int T, d, N, E, k;
 };
-constexpr int kDecodeMaxPairs = 4096;
+// The decode path handles at most this many tokens per call.
+constexpr int kDecodeMaxT = 256;
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 struct CombineArgs {

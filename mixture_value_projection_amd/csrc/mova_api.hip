@@ -17,8 +17,8 @@ using namespace mova;
 
 constexpr int kVersion = 100;  // 0.1.0
 constexpr int kMaxT = 1 << 24;
-// Token counts up to this take the weight-streaming decode path.
-constexpr int kDecodeMaxT = 64;
+// Token counts up to this take the weight-streaming decode path by default.
+constexpr int kDecodeAutoMaxT = 64;
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -43,20 +43,22 @@ int check_heads(int n_kv_heads, int head_dim) {
 enum class Path { Decode, Grouped };
 
 Path choose_path(int T, int k) {
+  (void)k;
   const char* force = getenv("MOVA_PATH");
-  const bool decode_ok = (long long)T * k <= kDecodeMaxPairs;
+  const bool decode_ok = T <= kDecodeMaxT;
   if (force != nullptr) {
     if (strcmp(force, "decode") == 0 && decode_ok) return Path::Decode;
     if (strcmp(force, "grouped") == 0) return Path::Grouped;
   }
-  return (T <= kDecodeMaxT && decode_ok) ? Path::Decode : Path::Grouped;
+  return (T <= kDecodeAutoMaxT && decode_ok) ? Path::Decode : Path::Grouped;
 }
 
 // Workspace layout (every region 256-byte aligned):
 //   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] i32 |
-//   tile_base [E+1] i32 | perm [T*k] i32 | partial [T*k*N] f32
+//   tile_base [E+1] i32 | plog (small-T router partial logits, T <= kDecodeMaxT
+//   only) | perm [T*k] i32 | partial [T*k*N] f32
 struct Layout {
-  size_t idx, w, chunk, eoff, tbase, perm, partial, total;
+  size_t idx, w, chunk, eoff, tbase, plog, perm, partial, total;
 };
 
 Layout layout(int T, int E, int k, int N) {
@@ -69,6 +71,7 @@ Layout layout(int T, int E, int k, int N) {
   L.chunk = o;   o += align256(C * E * 4);
   L.eoff = o;    o += align256((size_t)(E + 1) * 4);
   L.tbase = o;   o += align256((size_t)(E + 1) * 4);
+  L.plog = o;    o += T <= kDecodeMaxT ? align256((size_t)router_small_plog_floats(T) * 4) : 0;
   L.perm = o;    o += align256(pairs * 4);
   L.partial = o; o += align256(pairs * N * 4);
   L.total = o;
@@ -151,7 +154,9 @@ int mova_route(const void* x, const void* router_w, const float* router_b, int T
     return MOVA_ERR_INVALID_ARG;
   RouterArgs ra{(const __bf16*)x, (const __bf16*)router_w, router_b, T, d, E, k, scale,
                 topk_idx, topk_w, nullptr};
-  const bool wide = T > kDecodeMaxT;
+  // Routing alone has no workspace, so it uses the single-kernel router (same
+  // bits as the two-kernel small-T router of the decode path).
+  const bool wide = T > kDecodeAutoMaxT;
   return launch_router(ra, wide, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }
 
@@ -182,6 +187,7 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
   int32_t* chunk = (int32_t*)(ws + L.chunk);
   int32_t* eoff = (int32_t*)(ws + L.eoff);
   int32_t* tbase = (int32_t*)(ws + L.tbase);
+  float* plog = (float*)(ws + L.plog);
   int32_t* perm = (int32_t*)(ws + L.perm);
   float* partial = (float*)(ws + L.partial);
   const __bf16* xb = (const __bf16*)x;
@@ -194,7 +200,7 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w,
                   wide ? chunk : nullptr};
-    err = launch_router(ra, wide, stream);
+    err = wide ? launch_router(ra, true, stream) : launch_router_small(ra, plog, stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
 

@@ -43,3 +43,36 @@ def test_chunking_bitwise(T, chunk):
         fwd(g, x=g["x"][c0:c0 + chunk], out=parts[c0:c0 + chunk])
     torch.cuda.synchronize()
     assert torch.equal(whole, parts)
+
+
+@pytest.mark.parametrize("T", [64, 1000])
+def test_graph_replay_matches_eager(T):
+    """A captured call replays to the eager result every time, with eager work
+    and synchronisations between the replays (decode path at T=64, grouped
+    path at T=1000)."""
+    g = gpu_layer(T, seed=3)
+    ws = torch.empty(binding.workspace_bytes(T, 2560, 64, 4, 8, 128), dtype=torch.uint8, device=DEV)
+    eager = fwd_ws(g, ws).clone()
+    out = torch.empty_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd_ws(g, ws, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd_ws(g, ws, out)
+    for rep in range(4):
+        out.zero_()
+        other = fwd(gpu_layer(80, seed=rep))   # unrelated eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs"
+        del other
+
+
+def fwd_ws(g, ws, out=None):
+    return binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], 4, 2.5, 8, 128,
+                                 out=out, workspace=ws)
