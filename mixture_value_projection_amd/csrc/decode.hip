@@ -17,14 +17,10 @@
 // the batch's MFMAs read their token operand from LDS.  Tokens are handled 16
 // at a time (one MFMA row group); an expert with more than 16 tokens takes
 // several passes over its weights.  The epilogue writes w * SiLU(z) to the
-// pair's partial row, like the grouped GEMM.
-//
-// Fused combine: the E workgroups of one column slice each bump that slice's
-// arrival counter (agent-scope release after their partial rows are written);
-// the last to arrive acquires and sums the slice's k partials per token in slot
-// order into the bf16 output -- the same fixed-order sum as the combine kernel
-// of the grouped path, so both paths give identical bits.  The counters are
-// zeroed by the router earlier in the same call.
+// pair's partial row, like the grouped GEMM; the combine kernel then sums each
+// token's k partials in slot order, so both paths give identical bits.  (A
+// fused last-arriver combine was measured and rejected: the agent-scope release
+// each workgroup needs costs far more than the separate combine launch.)
 #include "common.h"
 #include "kernels.h"
 

@@ -34,8 +34,15 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   const int c0 = min(C, sub * per), c1 = min(C, c0 + per);
 
   int s = 0;
-  if (e < E)
-    for (int c = c0; c < c1; ++c) s += counts[(size_t)c * E + e];
+  if (e < E) {
+    for (int cb = c0; cb < c1; cb += 32) {
+      int v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s += v[i];
+    }
+  }
   part[e][sub] = s;
   __syncthreads();
   if (sub == 0) {
@@ -49,11 +56,18 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   }
   __syncthreads();
   if (e < E) {
+    // Rewrite counts as offsets; each block of 32 is loaded before any store so
+    // the loads are not serialised behind the stores.
     int run = part[e][sub];
-    for (int c = c0; c < c1; ++c) {
-      const int v = counts[(size_t)c * E + e];
-      counts[(size_t)c * E + e] = run;
-      run += v;
+    for (int cb = c0; cb < c1; cb += 32) {
+      int v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if (cb + i < c1) counts[(size_t)(cb + i) * E + e] = run;
+        run += v[i];
+      }
     }
   }
   if (threadIdx.x == 0) {

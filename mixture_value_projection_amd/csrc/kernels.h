@@ -24,6 +24,14 @@ hipError_t launch_router(const RouterArgs& a, bool wide, hipStream_t stream);
 // Same bits as launch_router.  plog: router_small_plog_floats(T) floats.
 int router_small_plog_floats(int T);
 hipError_t launch_router_small(const RouterArgs& a, float* plog, hipStream_t stream);
+// Large-T router: class partials with the router weight in LDS, then a
+// one-lane-per-token selection that also writes the dispatch histogram for
+// 256-token chunks.  Same bits as launch_router.  Needs d / 128 <= 32 (rounded
+// up); plog: router_big_plog_floats(T) floats.
+int router_big_supported(int d);
+int router_big_plog_floats(int T);
+constexpr int kBigRouterChunk = 256;
+hipError_t launch_router_big(const RouterArgs& a, float* plog, hipStream_t stream);
 
 struct DispatchArgs {
   const int32_t* idx;     // [T, k] routing

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -71,7 +72,12 @@ Layout layout(int T, int E, int k, int N) {
   L.chunk = o;   o += align256(C * E * 4);
   L.eoff = o;    o += align256((size_t)(E + 1) * 4);
   L.tbase = o;   o += align256((size_t)(E + 1) * 4);
-  L.plog = o;    o += T <= kDecodeMaxT ? align256((size_t)router_small_plog_floats(T) * 4) : 0;
+  {
+    size_t pl = 0;
+    if (T <= kDecodeMaxT) pl = (size_t)router_small_plog_floats(T);
+    if (T > kDecodeAutoMaxT) pl = std::max(pl, (size_t)router_big_plog_floats(T));
+    L.plog = o;  o += align256(pl * 4);
+  }
   L.perm = o;    o += align256(pairs * 4);
   L.partial = o; o += align256(pairs * N * 4);
   L.total = o;
@@ -195,12 +201,16 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
 
   const Path path = choose_path(T, k);
   const bool wide = path == Path::Grouped;
+  // Large-T router (weight slices in LDS) when the grouped path runs with more
+  // tokens than the decode path would take; its histogram chunks are 256 tokens.
+  const bool big = wide && T > kDecodeAutoMaxT && router_big_supported(d);
   hipError_t err;
   {
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w,
                   wide ? chunk : nullptr};
-    err = wide ? launch_router(ra, true, stream) : launch_router_small(ra, plog, stream);
+    err = !wide ? launch_router_small(ra, plog, stream)
+                : big ? launch_router_big(ra, plog, stream) : launch_router(ra, true, stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
 
@@ -211,8 +221,8 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
   } else {
     {
       StageScope sc(1, stream);
-      DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, router_tokens_per_block(true),
-                      gemm_block_m()};
+      DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k,
+                      big ? kBigRouterChunk : router_tokens_per_block(true), gemm_block_m()};
       err = launch_dispatch(dp, stream);
     }
     if (err != hipSuccess) return MOVA_ERR_HIP;
