@@ -3,48 +3,60 @@
 // With few tokens per expert the layer is bound by reading the touched
 // experts' weights (page "MoVA: routing the value vectors ...", section "So
 // what does it cost?": decode is memory-bound and reads four experts per
-// token).  Each workgroup owns one (expert, 64-column slice) and streams that
-// slice's 64 x d weights exactly once from HBM; the tokens that chose the
+// token).  Each workgroup owns one (expert, 128-column slice) and streams that
+// slice's 128 x d weights exactly once from HBM; the tokens that chose the
 // expert (at most a few dozen) ride along as the MFMA's other operand, read
 // from cache.  No dispatch kernel is needed: the workgroup finds its tokens by
 // scanning the [T, k] routing with wave ballots, which also keeps them in
 // pair order.
 //
-// Each wave owns 16 of the slice's columns; its 64 lanes read 16 rows x 64 B
-// per 32-wide k step.  The k loop runs in batches of kUnroll steps: a batch's
-// weight loads are issued first, then the token rows of the next batch are
-// copied into LDS (double-buffered, 16-byte chunks XOR-swizzled by row), then
-// the batch's MFMAs read their token operand from LDS.  Tokens are handled 16
-// at a time (one MFMA row group); an expert with more than 16 tokens takes
-// several passes over its weights.  The epilogue writes w * SiLU(z) to the
-// pair's partial row, like the grouped GEMM; the combine kernel then sums each
-// token's k partials in slot order, so both paths give identical bits.  (A
-// fused last-arriver combine was measured and rejected: the agent-scope release
-// each workgroup needs costs far more than the separate combine launch.)
+// Each wave owns 32 of the slice's columns as two 16-column MFMA groups that
+// share one token fragment; per 32-wide k step its 64 lanes read 2 x 16 rows x
+// 64 B of weights.  The k loop runs in batches of kUnroll steps with two
+// batches of weight loads in flight: while batch bt's MFMAs run, batch bt+1's
+// weights are already on their way; the token rows of batch bt+1 are fetched,
+// and after the MFMAs the consumed registers are refilled with batch bt+2.
+// Token rows go through LDS (double-buffered, 16-byte chunks XOR-swizzled by
+// row).  The first two weight batches are issued before the routing scan,
+// which they do not depend on; the scan reads every pair's expert id and
+// weight in one round trip, and keeps the weights in LDS for the epilogue.
+// Tokens are handled 16 at a time (one MFMA row group); an expert with more
+// than 16 tokens takes several passes over its weights.  The epilogue writes
+// w * SiLU(z) to the pair's partial row, like the grouped GEMM; the combine
+// kernel then sums each token's k partials in slot order, so both paths give
+// identical bits.  (A fused last-arriver combine was measured and rejected:
+// the agent-scope release each workgroup needs costs far more than the
+// separate combine launch.)
+//
+// 64 experts x 1024 columns is 512 workgroups of 4 waves: at two workgroups
+// per CU (up to 256 registers per lane) the whole grid is resident at once.
 #include "common.h"
 #include "kernels.h"
 
 namespace mova {
 
-constexpr int kSlice = 64;    // columns per workgroup
-constexpr int kUnroll = 8;    // k steps per batch
-constexpr int kRowBytes = kUnroll * 64;       // one token's k range per batch
-constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per staged row
+constexpr int kSlice = 128;   // columns per workgroup (32 per wave)
+constexpr int kGroups = 2;    // 16-column MFMA groups per wave
 
-
-__device__ __forceinline__ int xs_off(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
-}
-
-__global__ __launch_bounds__(256) void decode_kernel(
+// kUnroll: k steps per batch; it divides the step count d / 32 (8 when it
+// can, else 2, which always does since d % 64 == 0).
+template <int kUnroll>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
     float* __restrict__ partial, int T, int d, int N, int E, int k) {
+  constexpr int kRowBytes = kUnroll * 64;  // one token's k range per batch
+  constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per staged row
+  constexpr int kCopies = 16 * kChunks >= 256 ? 16 * kChunks / 256 : 1;  // chunks per thread
+  auto xs_off = [](int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); };
   __shared__ int plist[kDecodeMaxT];
+  __shared__ float wlist[kDecodeMaxT];
+  __shared__ int wave_hits[4];
   __shared__ __attribute__((aligned(16))) char xs[2][16 * kRowBytes];
-  __shared__ int count;
+  // Staging threads: those past the batch's 16 x kChunks chunks (kUnroll = 2)
+  // repeat the last chunk, which is harmless.
 
-  const int slices = N / kSlice;
+  const int slices = ceil_div(N, kSlice);
   const int e = blockIdx.x / slices;
   const int n0 = (blockIdx.x % slices) * kSlice;
   const int tid = threadIdx.x;
@@ -53,84 +65,133 @@ __global__ __launch_bounds__(256) void decode_kernel(
   const int q = lane >> 4, r16 = lane & 15;
   const int npairs = T * k;
 
-  // Pairs routed to this expert, in pair order (a token picks e at most once).
-  if (wave == 0) {
-    int c = 0;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int base = 0; base < npairs; base += 64) {
-      const int p = base + lane;
-      const bool hit = p < npairs && idx[p] == e;
-      const uint64_t m = __ballot(hit);
-      if (hit) plist[c + __popcll(m & lt_mask)] = p;
-      c += __popcll(m);
-    }
-    if (lane == 0) count = c;
+  // Column of each group; rows past N (N a multiple of 64 but not of 128)
+  // load a clamped row and are never stored.
+  int ncol[kGroups];
+  const bf16_t* wrow[kGroups];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    ncol[g] = n0 + wave * 32 + g * 16 + r16;
+    wrow[g] = W + ((size_t)e * N + min(ncol[g], N - 1)) * d + q * 8;
   }
-  __syncthreads();
-  const int ce = count;
+  const int nb = d / 32 / kUnroll;  // exact by the choice of kUnroll
+  static_assert((16 * kChunks) % 256 == 0 || 16 * kChunks < 256, "whole staging chunks per thread");
+  auto load_w = [&](Frag16 (&b)[kGroups][kUnroll], int bt) {
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const bf16_t* p = wrow[g] + (size_t)bt * kUnroll * 32;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) b[g][u].u = load16(p + u * 32);
+    }
+  };
+  Frag16 b0[kGroups][kUnroll], b1[kGroups][kUnroll];
+  load_w(b0, 0);
+  if (nb > 1) load_w(b1, 1);
 
-  const int n = n0 + wave * 16 + r16;
-  const bf16_t* wrow = W + ((size_t)e * N + n) * d + q * 8;
-  const int steps = d / 32;            // even, since d % 64 == 0
-  const int nb = ceil_div(steps, kUnroll);
-  static_assert(16 * kChunks == 2 * 256, "two 16-byte chunks per thread per batch");
+  // Pairs routed to this expert, in pair order (a token picks e at most once),
+  // with their routing weights, 256 pairs per round: each thread reads one
+  // pair's expert id and weight, and the hits are ranked by wave ballots.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int ce = 0;
+  for (int base = 0; base < npairs; base += 256) {
+    const int p = base + tid;
+    const bool in = p < npairs;
+    const int pe = in ? idx[p] : -1;
+    const float pwv = in ? topk_w[p] : 0.f;
+    const bool hit = pe == e;
+    const uint64_t mm = __ballot(hit);
+    if (lane == 0) wave_hits[wave] = __popcll(mm);
+    __syncthreads();
+    int before = ce;
+    for (int w = 0; w < wave; ++w) before += wave_hits[w];
+    if (hit) {
+      const int slot = before + __popcll(mm & lt_mask);
+      plist[slot] = p;
+      wlist[slot] = pwv;
+    }
+    ce += (wave_hits[0] + wave_hits[1]) + (wave_hits[2] + wave_hits[3]);
+    __syncthreads();
+  }
 
   for (int p0 = 0; p0 < ce; p0 += 16) {
-    const bf16_t* src[2];
-    int cp_row[2], cp_ch[2];
+    if (p0 > 0) {
+      load_w(b0, 0);
+      if (nb > 1) load_w(b1, 1);
+    }
+    const bf16_t* src[kCopies];
+    int cp_row[kCopies], cp_ch[kCopies];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * 256;
+    for (int i = 0; i < kCopies; ++i) {
+      const int c = min(tid + i * 256, 16 * kChunks - 1);
       cp_row[i] = c / kChunks;
       cp_ch[i] = c % kChunks;
       const int pair = plist[min(p0 + cp_row[i], ce - 1)];
       src[i] = x + (size_t)(pair / k) * d;
     }
-    // Copy batch bt of the 16 token rows into xs[buf].  k offsets past the end
-    // of the row (d not a multiple of the batch) read a clamped address and
-    // store zeros, so those steps contribute nothing.
-    auto stage = [&](int bt, int buf) {
+    // Token-row chunks of batch bt.
+    auto load_x = [&](u32x4 (&v)[kCopies], int bt) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int kk = bt * kUnroll * 32 + cp_ch[i] * 8;
-        u32x4 v = load16(src[i] + min(kk, d - 8));
-        if (kk >= d) v = u32x4{0u, 0u, 0u, 0u};
-        store16(&xs[buf][xs_off(cp_row[i], cp_ch[i])], v);
-      }
+      for (int i = 0; i < kCopies; ++i) v[i] = load16(src[i] + bt * kUnroll * 32 + cp_ch[i] * 8);
     };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    stage(0, 0);
-    __syncthreads();
-    for (int bt = 0; bt < nb; ++bt) {
-      const int buf = bt & 1;
-      Frag16 b[kUnroll];
+    auto store_x = [&](const u32x4 (&v)[kCopies], int buf) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) b[u].u = load16(wrow + min(bt * kUnroll + u, steps - 1) * 32);
-      if (bt + 1 < nb) stage(bt + 1, buf ^ 1);
+      for (int i = 0; i < kCopies; ++i) store16(&xs[buf][xs_off(cp_row[i], cp_ch[i])], v[i]);
+    };
+    f32x4 acc[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    {
+      u32x4 v[kCopies];
+      load_x(v, 0);
+      store_x(v, 0);
+    }
+    __syncthreads();
+    // One batch: fetch batch bt+1's token rows, run batch bt's MFMAs from bc
+    // (the other buffer already holds or awaits batch bt+1's weights), refill
+    // bc with batch bt+2's weights, then publish bt+1's token rows.
+    auto batch = [&](int bt, Frag16 (&bc)[kGroups][kUnroll]) {
+      const int buf = bt & 1;
+      const bool more = bt + 1 < nb;
+      u32x4 v[kCopies];
+      if (more) load_x(v, bt + 1);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         Frag16 a;
         a.u = load16(&xs[buf][xs_off(r16, u * 4 + q)]);
-        acc = mfma16x16x32(a.h, b[u].h, acc);
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) acc[g] = mfma16x16x32(a.h, bc[g][u].h, acc[g]);
       }
+      if (bt + 2 < nb) load_w(bc, bt + 2);
+      if (more) store_x(v, buf ^ 1);
       __syncthreads();
+    };
+    for (int bt = 0; bt < nb; bt += 2) {
+      batch(bt, b0);
+      if (bt + 1 < nb) batch(bt + 1, b1);
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int r = p0 + q * 4 + v;
       if (r < ce) {
-        const int pair = plist[r];
-        partial[(size_t)pair * N + n] = topk_w[pair] * siluf(acc[v]);
+        const float wt = wlist[r];
+        float* dst = partial + (size_t)plist[r] * N;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+          if (ncol[g] < N) dst[ncol[g]] = wt * siluf(acc[g][v]);
       }
     }
   }
-
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.E * (a.N / kSlice));
-  decode_kernel<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
-                                          a.E, a.k);
+  const dim3 grid(a.E * ceil_div(a.N, kSlice));
+  if ((a.d / 32) % 8 == 0) {
+    decode_kernel<8><<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
+                                               a.E, a.k);
+  } else {
+    decode_kernel<2><<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
+                                               a.E, a.k);
+  }
   return hipGetLastError();
 }
 

@@ -21,65 +21,75 @@
 namespace mova {
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanSub = kScanThreads / kMaxExperts;  // threads per expert
+constexpr int kScanWaves = kScanThreads / 64;
 
+// One workgroup; lane = expert, so every count load is a contiguous row of
+// the [C, E] table.  Wave w owns chunks [w * per, (w + 1) * per).
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     int32_t* __restrict__ counts, int C, int E, int block_m,
     int32_t* __restrict__ expert_off, int32_t* __restrict__ tile_base) {
-  __shared__ int part[kMaxExperts][kScanSub];
+  __shared__ int wave_sum[kScanWaves][kMaxExperts];
   __shared__ int total[kMaxExperts];
-  const int e = threadIdx.x / kScanSub;
-  const int sub = threadIdx.x % kScanSub;
-  const int per = ceil_div(C, kScanSub);
-  const int c0 = min(C, sub * per), c1 = min(C, c0 + per);
+  __shared__ int mtiles[kMaxExperts];
+  const int e = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int per = ceil_div(C, kScanWaves);
+  const int c0 = min(C, w * per), c1 = min(C, c0 + per);
+  const bool live = e < E;
 
   int s = 0;
-  if (e < E) {
-    for (int cb = c0; cb < c1; cb += 32) {
-      int v[32];
+  if (live) {
+    for (int cb = c0; cb < c1; cb += 16) {
+      int v[16];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
+      for (int i = 0; i < 16; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) s += v[i];
+      for (int i = 0; i < 16; ++i) s += v[i];
     }
   }
-  part[e][sub] = s;
+  wave_sum[w][e] = s;
   __syncthreads();
-  if (sub == 0) {
-    int run = 0;
-    for (int i = 0; i < kScanSub; ++i) {
-      const int v = part[e][i];
-      part[e][i] = run;
-      run += v;
-    }
-    total[e] = e < E ? run : 0;
+  int run = 0;
+  for (int i = 0; i < w; ++i) run += wave_sum[i][e];
+  if (w == kScanWaves - 1) {
+    total[e] = live ? run + s : 0;
+    mtiles[e] = live ? ceil_div(run + s, block_m) : 0;
   }
-  __syncthreads();
-  if (e < E) {
-    // Rewrite counts as offsets; each block of 32 is loaded before any store so
-    // the loads are not serialised behind the stores.
-    int run = part[e][sub];
-    for (int cb = c0; cb < c1; cb += 32) {
-      int v[32];
+  // Rewrite counts as offsets; each block of 16 is loaded before any store.
+  if (live) {
+    for (int cb = c0; cb < c1; cb += 16) {
+      int v[16];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
+      for (int i = 0; i < 16; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
+      for (int i = 0; i < 16; ++i) {
         if (cb + i < c1) counts[(size_t)(cb + i) * E + e] = run;
         run += v[i];
       }
     }
   }
-  if (threadIdx.x == 0) {
-    int off = 0, tiles = 0;
-    for (int i = 0; i < E; ++i) {
-      expert_off[i] = off;
-      tile_base[i] = tiles;
-      off += total[i];
-      tiles += ceil_div(total[i], block_m);
+  __syncthreads();
+  if (w == 0) {
+    // Expert offsets and first M-tiles: lane e sums the experts before it
+    // (entries past E are zero).
+    int off = 0, tiles = 0, all = 0, all_tiles = 0;
+#pragma unroll 16
+    for (int i = 0; i < kMaxExperts; ++i) {
+      const int t = total[i];
+      const int mt = mtiles[i];
+      off += i < e ? t : 0;
+      tiles += i < e ? mt : 0;
+      all += t;
+      all_tiles += mt;
     }
-    expert_off[E] = off;
-    tile_base[E] = tiles;
+    if (e < E) {
+      expert_off[e] = off;
+      tile_base[e] = tiles;
+    }
+    if (e == 0) {
+      expert_off[E] = all;
+      tile_base[E] = all_tiles;
+    }
   }
 }
 

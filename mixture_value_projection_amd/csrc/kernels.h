@@ -17,21 +17,15 @@ struct RouterArgs {
   int32_t* chunk_counts;  // [blocks, E] or null
 };
 
-// Router blocks cover 16 tokens ("narrow", small T) or 64 ("wide").
-int router_tokens_per_block(bool wide);
-hipError_t launch_router(const RouterArgs& a, bool wide, hipStream_t stream);
+// Tile router: one workgroup per router_tile_tokens(T) tokens, top-k fused;
+// with chunk_counts set, each workgroup writes its per-expert pair counts
+// ([blocks, E]), so the dispatch chunk is router_tile_tokens(T) tokens.
+int router_tile_tokens(int T);
+hipError_t launch_router_tile(const RouterArgs& a, hipStream_t stream);
 // Small-T router: partial logits over many single-wave blocks, then top-k.
-// Same bits as launch_router.  plog: router_small_plog_floats(T) floats.
+// Same bits as launch_router_tile.  plog: router_small_plog_floats(T) floats.
 int router_small_plog_floats(int T);
 hipError_t launch_router_small(const RouterArgs& a, float* plog, hipStream_t stream);
-// Large-T router: class partials with the router weight in LDS, then a
-// one-lane-per-token selection that also writes the dispatch histogram for
-// 256-token chunks.  Same bits as launch_router.  Needs d / 128 <= 32 (rounded
-// up); plog: router_big_plog_floats(T) floats.
-int router_big_supported(int d);
-int router_big_plog_floats(int T);
-constexpr int kBigRouterChunk = 256;
-hipError_t launch_router_big(const RouterArgs& a, float* plog, hipStream_t stream);
 
 struct DispatchArgs {
   const int32_t* idx;     // [T, k] routing

@@ -58,13 +58,14 @@ Path choose_path(int T, int k) {
 //   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] i32 |
 //   tile_base [E+1] i32 | plog (small-T router partial logits, T <= kDecodeMaxT
 //   only) | perm [T*k] i32 | partial [T*k*N] f32
+// C = number of tile-router workgroups (dispatch chunks).
 struct Layout {
   size_t idx, w, chunk, eoff, tbase, plog, perm, partial, total;
 };
 
 Layout layout(int T, int E, int k, int N) {
   const size_t pairs = (size_t)T * k;
-  const size_t C = (size_t)ceil_div(T, router_tokens_per_block(true));
+  const size_t C = (size_t)ceil_div(T, router_tile_tokens(T));
   Layout L;
   size_t o = 0;
   L.idx = o;     o += align256(pairs * 4);
@@ -72,12 +73,7 @@ Layout layout(int T, int E, int k, int N) {
   L.chunk = o;   o += align256(C * E * 4);
   L.eoff = o;    o += align256((size_t)(E + 1) * 4);
   L.tbase = o;   o += align256((size_t)(E + 1) * 4);
-  {
-    size_t pl = 0;
-    if (T <= kDecodeMaxT) pl = (size_t)router_small_plog_floats(T);
-    if (T > kDecodeAutoMaxT) pl = std::max(pl, (size_t)router_big_plog_floats(T));
-    L.plog = o;  o += align256(pl * 4);
-  }
+  L.plog = o;    o += align256(T <= kDecodeMaxT ? (size_t)router_small_plog_floats(T) * 4 : 0);
   L.perm = o;    o += align256(pairs * 4);
   L.partial = o; o += align256(pairs * N * 4);
   L.total = o;
@@ -160,10 +156,9 @@ int mova_route(const void* x, const void* router_w, const float* router_b, int T
     return MOVA_ERR_INVALID_ARG;
   RouterArgs ra{(const __bf16*)x, (const __bf16*)router_w, router_b, T, d, E, k, scale,
                 topk_idx, topk_w, nullptr};
-  // Routing alone has no workspace, so it uses the single-kernel router (same
-  // bits as the two-kernel small-T router of the decode path).
-  const bool wide = T > kDecodeAutoMaxT;
-  return launch_router(ra, wide, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+  // Routing alone has no workspace, so it uses the single-kernel tile router
+  // (same bits as the two-kernel small-T router of the decode path).
+  return launch_router_tile(ra, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }
 
 int mova_value_forward(const void* x, const void* router_w, const float* router_b,
@@ -200,17 +195,13 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
   const __bf16* wb = (const __bf16*)expert_w;
 
   const Path path = choose_path(T, k);
-  const bool wide = path == Path::Grouped;
-  // Large-T router (weight slices in LDS) when the grouped path runs with more
-  // tokens than the decode path would take; its histogram chunks are 256 tokens.
-  const bool big = wide && T > kDecodeAutoMaxT && router_big_supported(d);
+  const bool grouped = path == Path::Grouped;
   hipError_t err;
   {
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w,
-                  wide ? chunk : nullptr};
-    err = !wide ? launch_router_small(ra, plog, stream)
-                : big ? launch_router_big(ra, plog, stream) : launch_router(ra, true, stream);
+                  grouped ? chunk : nullptr};
+    err = grouped ? launch_router_tile(ra, stream) : launch_router_small(ra, plog, stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
 
@@ -222,7 +213,7 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
     {
       StageScope sc(1, stream);
       DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k,
-                      big ? kBigRouterChunk : router_tokens_per_block(true), gemm_block_m()};
+                      router_tile_tokens(T), gemm_block_m()};
       err = launch_dispatch(dp, stream);
     }
     if (err != hipSuccess) return MOVA_ERR_HIP;

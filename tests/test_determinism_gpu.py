@@ -34,7 +34,9 @@ def test_repeat_and_stream_bitwise():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
-@pytest.mark.parametrize("T,chunk", [(4096, 512), (256, 64), (130, 13)])
+# The router's workgroup shape depends on the call's token count (16, 32 or 64
+# tokens per workgroup); (8192, 4096) and (17000, 4250) cross those shapes.
+@pytest.mark.parametrize("T,chunk", [(4096, 512), (256, 64), (130, 13), (8192, 4096), (17000, 4250)])
 def test_chunking_bitwise(T, chunk):
     g = gpu_layer(T, seed=T)
     whole = fwd(g).clone()
@@ -43,6 +45,15 @@ def test_chunking_bitwise(T, chunk):
         fwd(g, x=g["x"][c0:c0 + chunk], out=parts[c0:c0 + chunk])
     torch.cuda.synchronize()
     assert torch.equal(whole, parts)
+
+
+@pytest.mark.parametrize("T,chunk", [(20000, 3000), (40000, 12000)])
+def test_route_chunking_bitwise(T, chunk):
+    g = gpu_layer(T, seed=T)
+    idx, w = binding.route(g["x"], g["router_w"], g["router_b"], 4, 2.5)
+    for c0 in range(0, T, chunk):
+        i2, w2 = binding.route(g["x"][c0:c0 + chunk], g["router_w"], g["router_b"], 4, 2.5)
+        assert torch.equal(idx[c0:c0 + chunk], i2) and torch.equal(w[c0:c0 + chunk], w2)
 
 
 @pytest.mark.parametrize("T", [64, 1000])
