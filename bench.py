@@ -16,9 +16,11 @@ bytes = touched experts' weights once + router weights + x + out.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -171,6 +173,47 @@ def prefill_line(name, r):
     }
 
 
+# HBM traffic of the decode kernel, measured by rocprofv3 counter passes and
+# recorded with the hash of the kernel's sources; reported only while those
+# sources are unchanged.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_kernel_T64_traffic.md")
+DECODE_SOURCES = [os.path.join(ROOT, "mixture_value_projection_amd", "csrc", f)
+                  for f in ("decode.hip", "common.h")]
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """Bytes per launch from the committed counter record, or None."""
+    try:
+        with open(TRAFFIC_RECORD) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    m = re.search(r"traffic-record: source_sha256=([0-9a-f]+) traffic_bytes=(\d+)", text)
+    if m is None or m.group(1) != decode_source_hash():
+        return None
+    return int(m.group(2))
+
+
+def copy_calibration(mib, reps=5):
+    """Plain device-to-device copies of a known size (a reference for HBM counters)."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=DEV).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {n} bytes")
+
+
 def cpu_baseline(seconds_target=12.0):
     """The CPU oracle on the decode workload's tokens, repeated for ~seconds_target."""
     sys.path.insert(0, ROOT)
@@ -206,6 +249,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated per step")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run plain device copies of MIB MiB (reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): this library has no "
@@ -251,10 +296,13 @@ def main():
                        "bytes": call_bytes},
         "roofline": {"kernel": "decode_kernel (expert weight stream)", "bound": "hbm",
                      "achieved": achieved, "peak": accounting.HBM_PEAK_BPS / 1e9, "unit": "GB/s",
-                     "frac": achieved * 1e9 / accounting.HBM_PEAK_BPS, "traffic": None,
+                     "frac": achieved * 1e9 / accounting.HBM_PEAK_BPS,
+                     "traffic": recorded_traffic(),
                      "bytes_per_launch": kern_bytes, "avg_launch_us": 1e3 * r["stage_ms"],
                      "launches_timed": r["stage_records"]},
     }
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
     if not args.headline_only:
         sec = []
         for name in ("prefill", "skewed"):
