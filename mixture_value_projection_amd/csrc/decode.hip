@@ -12,18 +12,19 @@
 //
 // Each wave owns 32 of the slice's columns as two 16-column MFMA groups that
 // share one token fragment; per 32-wide k step its 64 lanes read 2 x 16 rows x
-// 64 B of weights.  The k loop runs in batches of kUnroll steps with two
-// batches of weight loads in flight: while batch bt's MFMAs run, batch bt+1's
-// weights are already on their way; the token rows of batch bt+1 are fetched,
-// and after the MFMAs the consumed registers are refilled with batch bt+2.
-// Token rows go through LDS (double-buffered, 16-byte chunks XOR-swizzled by
-// row).  The first two weight batches are issued before the routing scan,
-// which they do not depend on; the scan reads every pair's expert id and
-// weight in one round trip, and keeps the weights in LDS for the epilogue.
-// Tokens are handled 16 at a time (one MFMA row group); an expert with more
-// than 16 tokens takes several passes over its weights.  The epilogue writes
-// w * SiLU(z) to the pair's partial row, like the grouped GEMM; the combine
-// kernel then sums each token's k partials in slot order, so both paths give
+// 64 B of weights and one 16-byte token fragment (token row = lane % 16, read
+// straight from cache: the rows are a few hundred KB shared by the whole
+// grid).  The k loop runs in batches of kUnroll steps over a ring of three
+// register buffers, so three batches of loads are in flight while a batch's
+// MFMAs run; the waves never wait for each other inside the loop.  The first
+// two weight batches are issued before the routing scan, which they do not
+// depend on; the scan reads every pair's expert id and weight in one round
+// trip, and keeps the weights in LDS for the epilogue.  Tokens are handled 16
+// at a time (one MFMA row group); an expert with more than 16 tokens takes
+// several passes over its weights.  The epilogue writes w * SiLU(z) to the
+// pair's partial row, like the grouped GEMM; the combine kernel then sums each
+// token's k partials in slot order.  The MFMA chain of every (token, column)
+// runs over the k steps in order, as in the grouped GEMM, so both paths give
 // identical bits.  (A fused last-arriver combine was measured and rejected:
 // the agent-scope release each workgroup needs costs far more than the
 // separate combine launch.)
@@ -38,23 +39,16 @@ namespace mova {
 constexpr int kSlice = 128;   // columns per workgroup (32 per wave)
 constexpr int kGroups = 2;    // 16-column MFMA groups per wave
 
-// kUnroll: k steps per batch; it divides the step count d / 32 (8 when it
+// kUnroll: k steps per batch; it divides the step count d / 32 (4 when it
 // can, else 2, which always does since d % 64 == 0).
 template <int kUnroll>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
     float* __restrict__ partial, int T, int d, int N, int E, int k) {
-  constexpr int kRowBytes = kUnroll * 64;  // one token's k range per batch
-  constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per staged row
-  constexpr int kCopies = 16 * kChunks >= 256 ? 16 * kChunks / 256 : 1;  // chunks per thread
-  auto xs_off = [](int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & 7)) << 4); };
   __shared__ int plist[kDecodeMaxT];
   __shared__ float wlist[kDecodeMaxT];
   __shared__ int wave_hits[4];
-  __shared__ __attribute__((aligned(16))) char xs[2][16 * kRowBytes];
-  // Staging threads: those past the batch's 16 x kChunks chunks (kUnroll = 2)
-  // repeat the last chunk, which is harmless.
 
   const int slices = ceil_div(N, kSlice);
   const int e = blockIdx.x / slices;
@@ -75,7 +69,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     wrow[g] = W + ((size_t)e * N + min(ncol[g], N - 1)) * d + q * 8;
   }
   const int nb = d / 32 / kUnroll;  // exact by the choice of kUnroll
-  static_assert((16 * kChunks) % 256 == 0 || 16 * kChunks < 256, "whole staging chunks per thread");
   auto load_w = [&](Frag16 (&b)[kGroups][kUnroll], int bt) {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
@@ -84,7 +77,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int u = 0; u < kUnroll; ++u) b[g][u].u = load16(p + u * 32);
     }
   };
-  Frag16 b0[kGroups][kUnroll], b1[kGroups][kUnroll];
+  Frag16 b0[kGroups][kUnroll], b1[kGroups][kUnroll], b2[kGroups][kUnroll];
   load_w(b0, 0);
   if (nb > 1) load_w(b1, 1);
 
@@ -118,56 +111,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       load_w(b0, 0);
       if (nb > 1) load_w(b1, 1);
     }
-    const bf16_t* src[kCopies];
-    int cp_row[kCopies], cp_ch[kCopies];
+    // MFMA row r16 is pair p0 + r16 (rows past the expert's pairs repeat its
+    // last pair and are never stored).
+    const bf16_t* xr = x + (size_t)(plist[min(p0 + r16, ce - 1)] / k) * d + q * 8;
+    auto load_x = [&](Frag16 (&f)[kUnroll], int bt) {
 #pragma unroll
-    for (int i = 0; i < kCopies; ++i) {
-      const int c = min(tid + i * 256, 16 * kChunks - 1);
-      cp_row[i] = c / kChunks;
-      cp_ch[i] = c % kChunks;
-      const int pair = plist[min(p0 + cp_row[i], ce - 1)];
-      src[i] = x + (size_t)(pair / k) * d;
+      for (int u = 0; u < kUnroll; ++u) f[u].u = load16(xr + (bt * kUnroll + u) * 32);
+    };
+    Frag16 x0[kUnroll], x1[kUnroll], x2[kUnroll];
+    load_x(x0, 0);
+    if (nb > 1) load_x(x1, 1);
+    if (nb > 2) {
+      load_w(b2, 2);
+      load_x(x2, 2);
     }
-    // Token-row chunks of batch bt.
-    auto load_x = [&](u32x4 (&v)[kCopies], int bt) {
-#pragma unroll
-      for (int i = 0; i < kCopies; ++i) v[i] = load16(src[i] + bt * kUnroll * 32 + cp_ch[i] * 8);
-    };
-    auto store_x = [&](const u32x4 (&v)[kCopies], int buf) {
-#pragma unroll
-      for (int i = 0; i < kCopies; ++i) store16(&xs[buf][xs_off(cp_row[i], cp_ch[i])], v[i]);
-    };
     f32x4 acc[kGroups];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      u32x4 v[kCopies];
-      load_x(v, 0);
-      store_x(v, 0);
-    }
-    __syncthreads();
-    // One batch: fetch batch bt+1's token rows, run batch bt's MFMAs from bc
-    // (the other buffer already holds or awaits batch bt+1's weights), refill
-    // bc with batch bt+2's weights, then publish bt+1's token rows.
-    auto batch = [&](int bt, Frag16 (&bc)[kGroups][kUnroll]) {
-      const int buf = bt & 1;
-      const bool more = bt + 1 < nb;
-      u32x4 v[kCopies];
-      if (more) load_x(v, bt + 1);
+    // Batch bt's MFMAs from (bc, xc), then refill them with batch bt + 3.
+    auto batch = [&](int bt, Frag16 (&bc)[kGroups][kUnroll], Frag16 (&xc)[kUnroll]) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        Frag16 a;
-        a.u = load16(&xs[buf][xs_off(r16, u * 4 + q)]);
+      for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) acc[g] = mfma16x16x32(a.h, bc[g][u].h, acc[g]);
+        for (int g = 0; g < kGroups; ++g) acc[g] = mfma16x16x32(xc[u].h, bc[g][u].h, acc[g]);
+      if (bt + 3 < nb) {
+        load_w(bc, bt + 3);
+        load_x(xc, bt + 3);
       }
-      if (bt + 2 < nb) load_w(bc, bt + 2);
-      if (more) store_x(v, buf ^ 1);
-      __syncthreads();
     };
-    for (int bt = 0; bt < nb; bt += 2) {
-      batch(bt, b0);
-      if (bt + 1 < nb) batch(bt + 1, b1);
+    for (int bt = 0; bt < nb; bt += 3) {
+      batch(bt, b0, x0);
+      if (bt + 1 < nb) batch(bt + 1, b1, x1);
+      if (bt + 2 < nb) batch(bt + 2, b2, x2);
     }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -185,8 +160,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.E * ceil_div(a.N, kSlice));
-  if ((a.d / 32) % 8 == 0) {
-    decode_kernel<8><<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
+  if ((a.d / 32) % 4 == 0) {
+    decode_kernel<4><<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
                                                a.E, a.k);
   } else {
     decode_kernel<2><<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
