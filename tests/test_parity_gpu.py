@@ -80,7 +80,7 @@ RAGGED = [
     (129, 192, 5, 5, 1, 192),
     (300, 1024, 64, 4, 8, 128),
     (1000, 256, 64, 6, 2, 96),
-    (100, 8192, 16, 2, 1, 64),     # d beyond the LDS-slice router: single-kernel router
+    (100, 8192, 16, 2, 1, 64),     # long rows: 256 k steps
     (700, 320, 64, 3, 2, 64),      # router residue classes of unequal length
 ]
 
