@@ -100,9 +100,10 @@ int mova_route(const void* x, const void* router_w, const float* router_b,
  *   workspace    device scratch of at least mova_workspace_bytes(...) bytes,
  *                256-byte aligned; its contents on entry do not matter.
  *
- * Expert products accumulate in fp32; SiLU, weighting and the k-way sum are
- * fp32 in a fixed slot order (i = 0..k-1), rounded once to bf16 (nearest
- * even).  Results are bitwise reproducible for identical inputs and do not
+ * Expert products accumulate in fp32; SiLU and the routing weight are applied
+ * in fp32 and each slot's result is kept as fp16 (rounded to nearest even);
+ * the k-way sum is fp32 in a fixed slot order (i = 0..k-1), rounded once to
+ * bf16 (nearest even).  Results are bitwise reproducible for identical inputs and do not
  * depend on how the tokens are split across calls.
  */
 int mova_value_forward(const void* x, const void* router_w, const float* router_b,

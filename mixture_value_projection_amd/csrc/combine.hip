@@ -1,9 +1,9 @@
-// k-way combine: out[t, n] = sum_{i<k} partial[t * k + i, n], summed in slot
-// order i = 0 .. k-1 in fp32 and rounded once to bf16 (nearest even).  The
-// [T, N] result is the [T, n_kv_heads, head_dim] value tensor with column
-// n = h * head_dim + j (page "MoVA: routing the value vectors ...", section
-// "Where the routing happens": the mixture is summed per token and viewed as
-// heads of 128).
+// k-way combine: out[t, n] = sum_{i<k} partial[t * k + i, n], the fp16 slot
+// partials widened to fp32, summed in slot order i = 0 .. k-1 and rounded once
+// to bf16 (nearest even).  The [T, N] result is the [T, n_kv_heads, head_dim]
+// value tensor with column n = h * head_dim + j (page "MoVA: routing the
+// value vectors ...", section "Where the routing happens": the mixture is
+// summed per token and viewed as heads of 128).
 #include <algorithm>
 
 #include "common.h"
@@ -11,32 +11,26 @@
 
 namespace mova {
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+__global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ partial,
                                                       bf16_t* __restrict__ out, int T, int N, int k) {
   const int vec_per_row = N / 8;
   const long long total = (long long)T * vec_per_row;
   for (long long v = blockIdx.x * 256ll + threadIdx.x; v < total; v += (long long)gridDim.x * 256) {
     const long long t = v / vec_per_row;
     const int c = (int)(v % vec_per_row) * 8;
-    const float* src = partial + (size_t)t * k * N + c;
+    const f16_t* src = partial + (size_t)t * k * N + c;
     float s[8];
     {
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      const f16x8 h = __builtin_bit_cast(f16x8, load16(src));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] = lo[i];
-        s[i + 4] = hi[i];
-      }
+      for (int i = 0; i < 8; ++i) s[i] = (float)h[i];
     }
     for (int j = 1; j < k; ++j) {
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(src + (size_t)j * N);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + (size_t)j * N + 4);
+      const f16x8 h = __builtin_bit_cast(f16x8, load16(src + (size_t)j * N));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[i] += lo[i];
-        s[i + 4] += hi[i];
-      }
+      for (int i = 0; i < 8; ++i) s[i] += (float)h[i];
     }
     u32x4 packed;
 #pragma unroll

@@ -11,6 +11,7 @@ constexpr int kMaxExperts = 64;  // one wave lane per expert in the router
 constexpr int kMaxTopK = 8;
 
 typedef __bf16 bf16_t;
+typedef _Float16 f16_t;  // slot partials: w * SiLU(z) rounded once (nearest even)
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;

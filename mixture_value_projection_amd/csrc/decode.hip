@@ -21,11 +21,11 @@
 // depend on; the scan reads every pair's expert id and weight in one round
 // trip, and keeps the weights in LDS for the epilogue.  Tokens are handled 16
 // at a time (one MFMA row group); an expert with more than 16 tokens takes
-// several passes over its weights.  The epilogue writes w * SiLU(z) to the
-// pair's partial row, like the grouped GEMM; the combine kernel then sums each
-// token's k partials in slot order.  The MFMA chain of every (token, column)
-// runs over the k steps in order, as in the grouped GEMM, so both paths give
-// identical bits.  (A fused last-arriver combine was measured and rejected:
+// several passes over its weights.  The epilogue writes w * SiLU(z) (fp16,
+// rounded once) to the pair's partial row, like the grouped GEMM; the combine
+// kernel then sums each token's k partials in slot order.  The MFMA chain of
+// every (token, column) runs over the k steps in order, as in the grouped
+// GEMM, so both paths give identical bits.  (A fused last-arriver combine was measured and rejected:
 // the agent-scope release each workgroup needs costs far more than the
 // separate combine launch.)
 //
@@ -45,7 +45,7 @@ template <int kUnroll>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
-    float* __restrict__ partial, int T, int d, int N, int E, int k) {
+    f16_t* __restrict__ partial, int T, int d, int N, int E, int k) {
   __shared__ int plist[kDecodeMaxT];
   __shared__ float wlist[kDecodeMaxT];
   __shared__ int wave_hits[4];
@@ -149,10 +149,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int r = p0 + q * 4 + v;
       if (r < ce) {
         const float wt = wlist[r];
-        float* dst = partial + (size_t)plist[r] * N;
+        f16_t* dst = partial + (size_t)plist[r] * N;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
-          if (ncol[g] < N) dst[ncol[g]] = wt * siluf(acc[g][v]);
+          if (ncol[g] < N) dst[ncol[g]] = (f16_t)(wt * siluf(acc[g][v]));
       }
     }
   }

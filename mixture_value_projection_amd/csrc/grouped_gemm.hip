@@ -4,7 +4,8 @@
 // expert_off[e+1])) form the A operand by gathering token rows of x; the
 // expert's [N, d] weight (nn.Linear layout, k contiguous) is the B operand.
 // z = x_t W_e^T is accumulated in fp32 on bf16 MFMA, then
-// y = w[pair] * SiLU(z) is stored to the pair's own partial row
+// y = w[pair] * SiLU(z) is computed in fp32 and stored, rounded once to fp16,
+// to the pair's own partial row
 // (page "MoVA: routing the value vectors ...", section "Where the routing
 // happens": SiLU on each expert's output, weighted by the routing weight).
 // Each partial row is written by exactly one tile, so no atomics are needed;
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ perm, const float* __restrict__ topk_w,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_base,
-    float* __restrict__ partial, int d, int N, int E, int k) {
+    f16_t* __restrict__ partial, int d, int N, int E, int k) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];  // 2 stages
   __shared__ int tile_pair[BM];
   __shared__ float tile_w[BM];
@@ -183,10 +184,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       if (r < rows) {
         const int pair = tile_pair[r];
         const float wt = tile_w[r];
-        float* dst = partial + (size_t)pair * N + n0 + wn * 64 + r16;
+        f16_t* dst = partial + (size_t)pair * N + n0 + wn * 64 + r16;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (n0 + wn * 64 + j * 16 + r16 < N) dst[j * 16] = wt * siluf(acc[i][j][v]);
+          if (n0 + wn * 64 + j * 16 + r16 < N) dst[j * 16] = (f16_t)(wt * siluf(acc[i][j][v]));
         }
       }
     }

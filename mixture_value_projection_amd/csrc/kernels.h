@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace mova {
 
 struct RouterArgs {
@@ -46,7 +48,7 @@ struct GemmArgs {
   const float* topk_w;     // [T * k]
   const int32_t* expert_off;
   const int32_t* tile_base;
-  float* partial;          // [T * k, N]
+  f16_t* partial;          // [T * k, N]
   int T, d, N, E, k;
 };
 int gemm_block_m();
@@ -59,7 +61,7 @@ struct DecodeArgs {
   const __bf16* W;
   const int32_t* idx;   // [T, k]
   const float* topk_w;  // [T, k]
-  float* partial;       // [T * k, N]
+  f16_t* partial;       // [T * k, N]
   int T, d, N, E, k;
 };
 // The decode path handles at most this many tokens per call.
@@ -67,7 +69,7 @@ constexpr int kDecodeMaxT = 256;
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 struct CombineArgs {
-  const float* partial;  // [T * k, N]
+  const f16_t* partial;  // [T * k, N]
   __bf16* out;           // [T, N]
   int T, N, k;
 };

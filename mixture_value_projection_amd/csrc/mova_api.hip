@@ -57,7 +57,7 @@ Path choose_path(int T, int k) {
 // Workspace layout (every region 256-byte aligned):
 //   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] i32 |
 //   tile_base [E+1] i32 | plog (small-T router partial logits, T <= kDecodeMaxT
-//   only) | perm [T*k] i32 | partial [T*k*N] f32
+//   only) | perm [T*k] i32 | partial [T*k*N] f16
 // C = number of tile-router workgroups (dispatch chunks).
 struct Layout {
   size_t idx, w, chunk, eoff, tbase, plog, perm, partial, total;
@@ -75,7 +75,7 @@ Layout layout(int T, int E, int k, int N) {
   L.tbase = o;   o += align256((size_t)(E + 1) * 4);
   L.plog = o;    o += align256(T <= kDecodeMaxT ? (size_t)router_small_plog_floats(T) * 4 : 0);
   L.perm = o;    o += align256(pairs * 4);
-  L.partial = o; o += align256(pairs * N * 4);
+  L.partial = o; o += align256(pairs * N * 2);
   L.total = o;
   return L;
 }
@@ -190,7 +190,7 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
   int32_t* tbase = (int32_t*)(ws + L.tbase);
   float* plog = (float*)(ws + L.plog);
   int32_t* perm = (int32_t*)(ws + L.perm);
-  float* partial = (float*)(ws + L.partial);
+  f16_t* partial = (f16_t*)(ws + L.partial);
   const __bf16* xb = (const __bf16*)x;
   const __bf16* wb = (const __bf16*)expert_w;
 

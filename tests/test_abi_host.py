@@ -57,7 +57,7 @@ def test_workspace_bytes(lib):
     for T in (1, 16, 64, 65, 4096, 32768):
         n = binding.workspace_bytes(T, 2560, 64, 4, 8, 128)
         assert n > prev and n % 256 == 0
-        assert n >= T * 4 * 1024 * 4   # fp32 slot partials
+        assert n >= T * 4 * 1024 * 2   # fp16 slot partials
         prev = n
     bad = ctypes.c_size_t(-1).value
     assert lib.mova_workspace_bytes(16, 2560, 65, 4, 8, 128) == bad     # E > 64
