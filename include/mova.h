@@ -121,7 +121,8 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
  *
  * mova_timing_enable(capacity, stage_mask) starts a new collection
  * (capacity <= 0 or stage_mask == 0 turns timing off); it creates host-side
- * HIP events, no device memory.
+ * HIP events (timing-only: created without a system-scope fence, so they add
+ * no cache writeback around the stage), no device memory.
  * mova_timing_read waits for the recorded events and writes, for stage s < n,
  * the summed milliseconds to total_ms[s] and the number of recorded launches
  * to count[s].  Returns MOVA_OK, MOVA_ERR_INVALID_ARG or MOVA_ERR_HIP.

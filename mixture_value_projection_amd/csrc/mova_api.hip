@@ -239,7 +239,9 @@ int mova_timing_enable(int capacity, unsigned stage_mask) {
     if (!(stage_mask & (1u << s))) continue;
     g_timing.ev[s].resize(2 * (size_t)capacity, nullptr);
     for (auto& e : g_timing.ev[s]) {
-      if (hipEventCreate(&e) != hipSuccess) {
+      // Timing-only events: no system-scope fence around the stage, so the
+      // event pair brackets the kernels without a cache writeback of its own.
+      if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
         e = nullptr;
         timing_free();
         return MOVA_ERR_HIP;
