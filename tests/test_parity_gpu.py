@@ -103,6 +103,39 @@ def test_ragged_shapes_both_paths(T, d, E, k, H, D):
         assert torch.equal(a[0], b[0])
 
 
+def test_widest_output_both_paths():
+    """N at the top of the supported domain (128 heads x 128 = 16384 columns)."""
+    T, d, E, k, H, D = 70, 256, 4, 2, 128, 128
+    say(f"widest output T={T} d={d} E={E} k={k} N={H * D}")
+    g, sh = layer(T, d, E, k, H, D, seed=1601)
+    outs = {}
+    for path in ("grouped", "decode"):
+        out, idx, w = run_forward(g, k, 2.5, H, D, path)
+        st = P.full_check(g, k, 2.5, H, D, out, idx, w, what=f"{path} N={H * D}")
+        say(f"  {path}: {st}")
+        outs[path] = (out, idx, w)
+    a, b = outs["grouped"], outs["decode"]
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]) and torch.equal(a[0], b[0])
+
+
+def test_million_tokens():
+    """2^20 tokens in one call (narrow layer, k = 8): large grids, a 16K-chunk
+    dispatch table and 64-bit offsets.  Routing checked on every token, outputs
+    on a seeded sample plus every near-tie token."""
+    T, d, E, k, H, D = 1 << 20, 64, 64, 8, 1, 64
+    say(f"million tokens T={T} d={d} E={E} k={k} N={H * D}")
+    g, sh = layer(T, d, E, k, H, D, seed=2027)
+    out, idx, w = run_forward(g, k, 2.5, H, D)
+    o = P.oracle_inputs(g)
+    ref = oracle.route(o["x"], o["router_w"], o["router_b"], k, 2.5)
+    ties = np.nonzero(ref.margin <= P.MARGIN)[0][:4096]
+    rows = sample_rows(T, 2048, 13, extra=list(ties))
+    st = P.full_check(g, k, 2.5, H, D, out, idx, w, tokens=rows, ref=ref, what="2^20 tokens")
+    say(f"  rows={rows.size} {st}")
+    del out, idx, w, g
+    torch.cuda.empty_cache()
+
+
 def test_single_expert():
     g, sh = layer(40, 256, 1, 1, 2, 32, seed=1)
     for path in ("decode", "grouped"):
