@@ -17,8 +17,9 @@
 //
 // Kernels:
 //   router_tile_kernel     one workgroup per 16 * TG tokens, wave = class;
-//                          top-k and the per-chunk dispatch histogram in the
-//                          same kernel (large T, and routing-only calls);
+//                          selection (lane = token) and the per-chunk
+//                          dispatch histogram in the same kernel (large T,
+//                          and routing-only calls);
 //   router_partial_kernel  + router_topk_kernel: the same chains spread over
 //                          single-wave workgroups for small T.
 #include "common.h"
@@ -103,22 +104,60 @@ __device__ __forceinline__ void topk_tokens(const float (&logit)[NT], float b_la
   }
 }
 
+// One lane's running top-k list (slots 0 .. k-1 of KK >= k), ordered by
+// (selection score desc, expert index asc).  A candidate enters at the first
+// slot whose score it strictly exceeds, and everything from there shifts down
+// one slot (the carried entry ranks ahead of all later ones).  Candidates
+// offered in increasing expert index therefore keep the lower index first
+// among equal scores: the same order as topk_tokens.
+template <int KK>
+__device__ __forceinline__ void insert_ranked(float (&bv)[KK], float (&bs)[KK], int (&bi)[KK],
+                                              int k, float cv, float cs, int ci) {
+  bool moving = false;
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+    if (j < k && (moving || cv > bv[j])) {
+      const float tv = bv[j], ts = bs[j];
+      const int ti = bi[j];
+      bv[j] = cv;
+      bs[j] = cs;
+      bi[j] = ci;
+      cv = tv;
+      cs = ts;
+      ci = ti;
+      moving = true;
+    }
+  }
+}
+
 // ---- tile router: one workgroup per 16 * TG tokens ------------------------
 //
 // Wave rc (of 4) runs class rc's chains for all TG token groups against all
 // four expert blocks: per k step it loads one 16-byte token fragment per token
 // group and one router-weight fragment per expert block, U steps per batch,
-// all loads of a batch before its MFMAs.  Class partials meet in LDS; each
-// wave then selects for every fourth token of the tile.  A workgroup's tokens
-// form one dispatch chunk: when chunk_counts is given, it receives the
-// workgroup's per-expert pair counts.
-template <int TG, int U>
+// all loads of a batch before its MFMAs.  Class partials meet in LDS (rows
+// padded by one word so that a column read by 64 lanes hits 64 banks).
+// Selection: 16-token tiles use topk_tokens (lane = expert, four tokens per
+// wave); larger tiles run with lane = token: wave w keeps each token's top-k
+// over experts 16w .. 16w + 15 (offered in index order), and wave 0 merges
+// the other three waves' lists in wave order -- the same selection, order and
+// weight sum as topk_tokens, at a fraction of the cost per token.  A
+// workgroup's tokens form one dispatch chunk: when chunk_counts is given, it
+// receives the workgroup's per-expert pair counts.  KK: list length (k <= KK).
+template <int TG, int U, int KK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void router_tile_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int E, int k, float scale,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts) {
   constexpr int TM = 16 * TG;
-  __shared__ float part[4][TM][kMaxExperts];
+  constexpr int kQ = kMaxExperts / 4;       // experts per wave in the selection
+  constexpr int kPad = kMaxExperts + 1;
+  __shared__ float part[4][TM][kPad];
+  constexpr bool kLaneToken = TG > 1;        // selection with lane = token
+  constexpr int TC = kLaneToken ? TM : 1;
+  __shared__ float cand_v[3][KK][TC];       // selection lists of waves 1..3
+  __shared__ float cand_s[3][KK][TC];
+  __shared__ int cand_i[3][KK][TC];
   __shared__ int hist[kMaxExperts];
 
   const int lane = threadIdx.x & 63;
@@ -128,9 +167,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int t0 = blockIdx.x * TM;
 
   if (threadIdx.x < kMaxExperts) hist[threadIdx.x] = 0;
-  const float b_lane = (bias != nullptr && lane < E) ? bias[lane] : 0.f;
+  // Biases of this wave's selection experts (wave-uniform: scalar loads).
+  const int wq = __builtin_amdgcn_readfirstlane(rc);
+  float bq[kQ];
+#pragma unroll
+  for (int j = 0; j < kQ; ++j) bq[j] = (bias != nullptr && wq * kQ + j < E) ? bias[wq * kQ + j] : 0.f;
   // Token rows clamped into range (rows past T are never written); expert rows
-  // clamped (lanes for experts >= E are masked in top-k).
+  // clamped (experts >= E are never offered to the selection).
   const bf16_t* xrow[TG];
 #pragma unroll
   for (int g = 0; g < TG; ++g) xrow[g] = x + (size_t)min(t0 + g * 16 + r16, T - 1) * d + q * 8;
@@ -176,26 +219,83 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       for (int i = 0; i < 4; ++i) part[rc][g * 16 + q * 4 + i][eb * 16 + r16] = acc[g][eb][i];
   __syncthreads();
 
-  // Wave rc selects for tokens rc, rc + 4, ..., NT of them at a time.
-  constexpr int NT = TM / 4 < 4 ? TM / 4 : 4;
-  for (int r0 = rc; r0 < TM; r0 += 4 * NT) {
-    float logit[NT];
+  if constexpr (!kLaneToken) {
+    // 16-token tiles: lane = expert, wave rc selects for tokens rc, rc + 4,
+    // rc + 8, rc + 12 together (topk_tokens).
+    const float b_lane = (bias != nullptr && lane < E) ? bias[lane] : 0.f;
+    float logit[4];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int r = min(r0 + 4 * i, TM - 1);
+    for (int i = 0; i < 4; ++i) {
+      const int r = rc + 4 * i;
       logit[i] = ((part[0][r][lane] + part[1][r][lane]) + part[2][r][lane]) + part[3][r][lane];
     }
-    int my_idx[NT];
-    float my_w[NT];
-    topk_tokens<NT>(logit, b_lane, lane, E, k, scale, my_idx, my_w);
+    int my_idx[4];
+    float my_w[4];
+    topk_tokens<4>(logit, b_lane, lane, E, k, scale, my_idx, my_w);
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int r = r0 + 4 * i;
-      const int t = t0 + r;
-      if (r < TM && t < T && lane < k) {
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + rc + 4 * i;
+      if (t < T && lane < k) {
         idx_out[(size_t)t * k + lane] = my_idx[i];
         w_out[(size_t)t * k + lane] = my_w[i];
         if (chunk_counts != nullptr) atomicAdd(&hist[my_idx[i]], 1);
+      }
+    }
+  } else {
+    // Larger tiles: lane = token (row `lane` of the tile).
+    float bv[KK], bs[KK];
+    int bi[KK];
+#pragma unroll
+    for (int j = 0; j < KK; ++j) {
+      bv[j] = -__builtin_inff();
+      bs[j] = 0.f;
+      bi[j] = 0;
+    }
+    if (lane < TM) {
+#pragma unroll
+      for (int j = 0; j < kQ; ++j) {
+        const int e = wq * kQ + j;
+        if (e < E) {
+          const float logit =
+              ((part[0][lane][e] + part[1][lane][e]) + part[2][lane][e]) + part[3][lane][e];
+          const float sc = sigmoidf_fast(logit);
+          insert_ranked<KK>(bv, bs, bi, k, sc + bq[j], sc, e);
+        }
+      }
+      if (rc > 0) {
+#pragma unroll
+        for (int j = 0; j < KK; ++j) {
+          cand_v[rc - 1][j][lane] = bv[j];
+          cand_s[rc - 1][j][lane] = bs[j];
+          cand_i[rc - 1][j][lane] = bi[j];
+        }
+      }
+    }
+    __syncthreads();
+    if (rc == 0 && lane < TM) {
+#pragma unroll
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int j = 0; j < KK; ++j)
+          if (j < k)
+            insert_ranked<KK>(bv, bs, bi, k, cand_v[w][j][lane], cand_s[w][j][lane], cand_i[w][j][lane]);
+      float ssum = 0.f;
+#pragma unroll
+      for (int j = 0; j < KK; ++j)
+        if (j < k) ssum += bs[j];
+      const int t = t0 + lane;
+      if (t < T) {
+#pragma unroll
+        for (int j = 0; j < KK; ++j) {
+          if (j < k) {
+            // Clamped so that even non-finite scores (undefined results) can
+            // never produce an out-of-range expert index.
+            const int e = min(max(bi[j], 0), E - 1);
+            idx_out[(size_t)t * k + j] = e;
+            w_out[(size_t)t * k + j] = scale * bs[j] / ssum;
+            if (chunk_counts != nullptr) atomicAdd(&hist[e], 1);
+          }
+        }
       }
     }
   }
@@ -210,17 +310,19 @@ int router_tile_tokens(int T) { return T <= 8192 ? 16 : T <= 16384 ? 32 : 64; }
 hipError_t launch_router_tile(const RouterArgs& a, hipStream_t stream) {
   const int TM = router_tile_tokens(a.T);
   const dim3 grid(ceil_div(a.T, TM));
+#define MOVA_ROUTER_TILE(TG, U, KK)                                                            \
+  router_tile_kernel<TG, U, KK><<<grid, 256, 0, stream>>>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k, \
+                                                          a.scale, a.idx, a.w, a.chunk_counts)
   // U: k steps per load batch (TG + 4 fragments of 4 registers each per step).
+  const bool small_k = a.k <= 4;
   if (TM == 16) {
-    router_tile_kernel<1, 10><<<grid, 256, 0, stream>>>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k,
-                                                       a.scale, a.idx, a.w, a.chunk_counts);
+    if (small_k) MOVA_ROUTER_TILE(1, 10, 4); else MOVA_ROUTER_TILE(1, 10, 8);
   } else if (TM == 32) {
-    router_tile_kernel<2, 5><<<grid, 256, 0, stream>>>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k,
-                                                      a.scale, a.idx, a.w, a.chunk_counts);
+    if (small_k) MOVA_ROUTER_TILE(2, 5, 4); else MOVA_ROUTER_TILE(2, 5, 8);
   } else {
-    router_tile_kernel<4, 2><<<grid, 256, 0, stream>>>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k,
-                                                      a.scale, a.idx, a.w, a.chunk_counts);
+    if (small_k) MOVA_ROUTER_TILE(4, 2, 4); else MOVA_ROUTER_TILE(4, 2, 8);
   }
+#undef MOVA_ROUTER_TILE
   return hipGetLastError();
 }
 
