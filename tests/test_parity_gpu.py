@@ -136,6 +136,38 @@ def test_million_tokens():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("T", [40, 600])
+def test_bias_omitted_equals_zero_bias(T):
+    """router_b = NULL means a zero bias: same bits as passing zeros, both paths."""
+    d, E, k, H, D = 512, 32, 4, 2, 64
+    g, sh = layer(T, d, E, k, H, D, seed=T + 5)
+    g_none = dict(g, router_b=None)
+    g_zero = dict(g, router_b=torch.zeros(E, dtype=torch.float32, device=DEV))
+    for path in ("grouped", "decode") if T <= 256 else ("grouped",):
+        a = run_forward(g_none, k, 2.5, H, D, path)
+        b = run_forward(g_zero, k, 2.5, H, D, path)
+        assert all(torch.equal(u, v) for u, v in zip(a, b)), path
+        st = P.full_check(g_none, k, 2.5, H, D, *a, what=f"{path} no bias")
+        say(f"  {path} T={T}: {st}")
+    i1, w1 = binding.route(g["x"], g["router_w"], None, k, 2.5)
+    i2, w2 = binding.route(g["x"], g["router_w"], g_zero["router_b"], k, 2.5)
+    assert torch.equal(i1, i2) and torch.equal(w1, w2)
+
+
+@pytest.mark.parametrize("T", [64, 1000])
+def test_power_of_two_scale_is_exact(T):
+    """Doubling the scale doubles weights and outputs bit for bit (every
+    rounding step, fp16 partials and the bf16 output included, commutes with
+    multiplication by 2)."""
+    d, E, k, H, D = 2560, 64, 4, 8, 128
+    g, sh = layer(T, d, E, k, H, D, seed=T + 9)
+    o1, i1, w1 = run_forward(g, k, 2.5, H, D)
+    o2, i2, w2 = run_forward(g, k, 5.0, H, D)
+    assert torch.equal(i1, i2)
+    assert torch.equal(w2, 2 * w1)
+    assert torch.equal(o2.float(), 2 * o1.float())
+
+
 def test_single_expert():
     g, sh = layer(40, 256, 1, 1, 2, 32, seed=1)
     for path in ("decode", "grouped"):
