@@ -20,8 +20,9 @@
 // two weight batches are issued before the routing scan, which they do not
 // depend on; the scan reads every pair's expert id and weight in one round
 // trip, and keeps the weights in LDS for the epilogue.  Tokens are handled 16
-// at a time (one MFMA row group); an expert with more than 16 tokens takes
-// several passes over its weights.  The epilogue writes w * SiLU(z) (fp16,
+// at a time (one MFMA row group), or 32 at a time (two row groups) when the
+// expert has more than 16; an expert with more than 32 tokens takes several
+// passes over its weights.  The epilogue writes w * SiLU(z) (fp16,
 // rounded once) to the pair's partial row, like the grouped GEMM; the combine
 // kernel then sums each token's k partials in slot order.  The MFMA chain of
 // every (token, column) runs over the k steps in order, as in the grouped
@@ -31,6 +32,8 @@
 //
 // 64 experts x 1024 columns is 512 workgroups of 4 waves: at two workgroups
 // per CU (up to 256 registers per lane) the whole grid is resident at once.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -40,8 +43,10 @@ constexpr int kSlice = 128;   // columns per workgroup (32 per wave)
 constexpr int kGroups = 2;    // 16-column MFMA groups per wave
 
 // kUnroll: k steps per batch; it divides the step count d / 32 (4 when it
-// can, else 2, which always does since d % 64 == 0).
-template <int kUnroll>
+// can, else 2, which always does since d % 64 == 0).  kPair32: experts with
+// more than 16 pairs use 32-pair passes (worth it beyond 64 tokens; without
+// it the kernel holds fewer registers, and such experts take 16-pair passes).
+template <int kUnroll, bool kPair32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
@@ -106,67 +111,90 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __syncthreads();
   }
 
-  for (int p0 = 0; p0 < ce; p0 += 16) {
+  // One pass over the weights for RG row groups of 16 pairs (pairs p0 ..
+  // p0 + 16 RG - 1); MFMA row r16 of group rg is pair p0 + 16 rg + r16, rows
+  // past the expert's pairs repeat its last pair and are never stored.
+  auto pass = [&](auto rg_tag, int p0) {
+    constexpr int RG = decltype(rg_tag)::value;
     if (p0 > 0) {
       load_w(b0, 0);
       if (nb > 1) load_w(b1, 1);
     }
-    // MFMA row r16 is pair p0 + r16 (rows past the expert's pairs repeat its
-    // last pair and are never stored).
-    const bf16_t* xr = x + (size_t)(plist[min(p0 + r16, ce - 1)] / k) * d + q * 8;
-    auto load_x = [&](Frag16 (&f)[kUnroll], int bt) {
+    const bf16_t* xr[RG];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) f[u].u = load16(xr + (bt * kUnroll + u) * 32);
+    for (int rg = 0; rg < RG; ++rg)
+      xr[rg] = x + (size_t)(plist[min(p0 + rg * 16 + r16, ce - 1)] / k) * d + q * 8;
+    auto load_x = [&](Frag16 (&f)[RG][kUnroll], int bt) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) f[rg][u].u = load16(xr[rg] + (bt * kUnroll + u) * 32);
     };
-    Frag16 x0[kUnroll], x1[kUnroll], x2[kUnroll];
+    // Ring of register batches: three deep for one row group, two for two
+    // (which holds twice the token fragments per batch).
+    constexpr int kRing = RG == 1 ? 3 : 2;
+    Frag16 x0[RG][kUnroll], x1[RG][kUnroll], x2[RG][kUnroll];
     load_x(x0, 0);
     if (nb > 1) load_x(x1, 1);
-    if (nb > 2) {
+    if (kRing == 3 && nb > 2) {
       load_w(b2, 2);
       load_x(x2, 2);
     }
-    f32x4 acc[kGroups];
+    f32x4 acc[RG][kGroups];
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Batch bt's MFMAs from (bc, xc), then refill them with batch bt + 3.
-    auto batch = [&](int bt, Frag16 (&bc)[kGroups][kUnroll], Frag16 (&xc)[kUnroll]) {
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) acc[rg][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Batch bt's MFMAs from (bc, xc), then refill them with batch bt + kRing.
+    auto batch = [&](int bt, Frag16 (&bc)[kGroups][kUnroll], Frag16 (&xc)[RG][kUnroll]) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) acc[g] = mfma16x16x32(xc[u].h, bc[g][u].h, acc[g]);
-      if (bt + 3 < nb) {
-        load_w(bc, bt + 3);
-        load_x(xc, bt + 3);
+        for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g)
+            acc[rg][g] = mfma16x16x32(xc[rg][u].h, bc[g][u].h, acc[rg][g]);
+      if (bt + kRing < nb) {
+        load_w(bc, bt + kRing);
+        load_x(xc, bt + kRing);
       }
     };
-    for (int bt = 0; bt < nb; bt += 3) {
+    for (int bt = 0; bt < nb; bt += kRing) {
       batch(bt, b0, x0);
       if (bt + 1 < nb) batch(bt + 1, b1, x1);
-      if (bt + 2 < nb) batch(bt + 2, b2, x2);
+      if (kRing == 3 && bt + 2 < nb) batch(bt + 2, b2, x2);
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int r = p0 + q * 4 + v;
-      if (r < ce) {
-        const float wt = wlist[r];
-        f16_t* dst = partial + (size_t)plist[r] * N;
+    for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
-          if (ncol[g] < N) dst[ncol[g]] = (f16_t)(wt * siluf(acc[g][v]));
+      for (int v = 0; v < 4; ++v) {
+        const int r = p0 + rg * 16 + q * 4 + v;
+        if (r < ce) {
+          const float wt = wlist[r];
+          f16_t* dst = partial + (size_t)plist[r] * N;
+#pragma unroll
+          for (int g = 0; g < kGroups; ++g)
+            if (ncol[g] < N) dst[ncol[g]] = (f16_t)(wt * siluf(acc[rg][g][v]));
+        }
       }
     }
+  };
+  // Experts with more than 16 pairs take 32 per pass (two row groups), so up
+  // to 32 pairs cost one pass over the weights.
+  if (!kPair32 || ce <= 16) {
+    for (int p0 = 0; p0 < ce; p0 += 16) pass(std::integral_constant<int, 1>{}, p0);
+  } else {
+    for (int p0 = 0; p0 < ce; p0 += 32) pass(std::integral_constant<int, 2>{}, p0);
   }
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.E * ceil_div(a.N, kSlice));
-  if ((a.d / 32) % 4 == 0) {
-    decode_kernel<4><<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
-                                               a.E, a.k);
-  } else {
-    decode_kernel<2><<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N,
-                                               a.E, a.k);
-  }
+  const bool unroll4 = (a.d / 32) % 4 == 0;
+  const bool pair32 = a.T > 64;
+  auto kern = unroll4 ? (pair32 ? decode_kernel<4, true> : decode_kernel<4, false>)
+                      : (pair32 ? decode_kernel<2, true> : decode_kernel<2, false>);
+  kern<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N, a.E, a.k);
   return hipGetLastError();
 }
 
