@@ -5,7 +5,9 @@ combine) on one batch of seeded synthetic tokens with inputs already resident
 in HBM.  The headline workload is the decode step (T=64, d=2560, 64 experts
 of 2560->1024, top-4, bf16); the prefill workloads (T=4096 chunk, T=32768
 skewed, 8x8192 chunked through 4 layers) are measured as secondary lines in
-the same JSON object unless --headline-only is given.
+the same JSON object unless --headline-only is given, and so is the matched
+dense GQA v_proj (one 2560->1024 weight, no routing) at each workload's
+token count, with the MoVA / dense time ratio.
 
 Layer weights are rotated over several copies (>= 1.3 GB in total) so the
 256 MB Infinity Cache cannot serve them between steps.
@@ -149,6 +151,49 @@ def run_chunked(steps, warmup):
                 calls=steps * w.chunks * w.layers, stage_ms=stage_ms, stage_records=nrec,
                 graph_seconds=gsecs, graph_calls=gsteps * w.chunks * w.layers,
                 graph_tokens=total * gsteps, graph_layer_tokens=total * w.layers * gsteps)
+
+
+def run_dense(name, steps, warmup, copies=64):
+    """The matched dense v_proj (one [N, d] weight) at a workload's token count.
+
+    The weight is rotated over `copies` device copies (64 x 5.2 MB > the 256 MB
+    Infinity Cache), as a model's other layers would evict it between calls.
+    hipBLASLt (torch.matmul) on the same operands is timed beside it as a
+    library reference."""
+    w = inputs.WORKLOADS[name]
+    sh = w.shape
+    x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
+    base = inputs.make_dense_vproj(sh, w.seed, w.dtype).to(DEV)
+    wts = [base] + [base.clone() for _ in range(copies - 1)]
+    out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+    wsb = binding.dense_workspace_bytes(sh.T, sh.d, sh.n_kv_heads, sh.head_dim)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    calls = [(lambda wt=wt: binding.dense_value_proj(x, wt, sh.n_kv_heads, sh.head_dim, out=out,
+                                                     workspace=ws)) for wt in wts]
+    n = max(steps, copies)
+    secs, stage_ms, nrec = timed_calls(calls, n, warmup, "dense")
+    gsecs, gcalls = graph_time(calls, n, warmup)
+    out2 = torch.empty(sh.T, sh.N, dtype=torch.bfloat16, device=DEV)
+    mm = [(lambda wt=wt: torch.matmul(x, wt.t(), out=out2)) for wt in wts]
+    msecs, mcalls = graph_time(mm, n, warmup)
+    del wts, calls, mm
+    return dict(T=sh.T, d=sh.d, N=sh.N, us=1e6 * gsecs / gcalls, kernel_us=1e3 * stage_ms,
+                launches_timed=nrec, hipblaslt_us=1e6 * msecs / mcalls)
+
+
+def dense_line(name, r, mova_us):
+    T, d, N = r["T"], r["d"], r["N"]
+    flops = 2.0 * T * d * N
+    nbytes = 2.0 * (N * d + T * d + T * N)
+    line = {"workload": name, "T": T, "dense_us": r["us"], "dense_call_events_us": r["kernel_us"],
+            "hipblaslt_us": r["hipblaslt_us"], "mova_us": mova_us,
+            "mova_over_dense": mova_us / r["us"],
+            "mova_over_hipblaslt": mova_us / r["hipblaslt_us"],
+            "dense_tflops": flops / (r["us"] * 1e-6) / 1e12,
+            "dense_frac_bf16_peak": flops / (r["us"] * 1e-6) / accounting.BF16_MFMA_PEAK_FLOPS,
+            "dense_GB_per_s": nbytes / (r["us"] * 1e-6) / 1e9,
+            "dense_frac_hbm": nbytes / (r["us"] * 1e-6) / accounting.HBM_PEAK_BPS}
+    return line
 
 
 def prefill_line(name, r):
@@ -318,6 +363,16 @@ def main():
         sec.append(prefill_line("chunked", rr))
         line["secondary"] = sec
         torch.cuda.empty_cache()
+        log("dense v_proj baseline ...")
+        mova_us = {"decode": 1e6 * step_s}
+        for d_ in sec:
+            mova_us[d_["workload"]] = 1e3 * d_["ms_per_call"]
+        gqa = []
+        for name in ("decode", "prefill", "skewed", "chunked"):
+            rr = run_dense(name, max(64, args.steps // 2), max(8, args.warmup))
+            gqa.append(dense_line(name, rr, mova_us[name]))
+            torch.cuda.empty_cache()
+        line["gqa_baseline"] = gqa
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline()

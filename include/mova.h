@@ -113,11 +113,45 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Bytes of device workspace mova_dense_value_proj needs for these sizes: 0
+ * when T == 0 or T > 256, (size_t)-1 outside the supported domain (that of
+ * mova_value_forward without the router's E and k).
+ */
+size_t mova_dense_workspace_bytes(int T, int d, int n_kv_heads, int head_dim);
+
+/*
+ * Plain (dense) GQA value projection, the matched baseline of the routed
+ * projection: the model's first dense layers keep an ordinary v_proj, a
+ * single bias-free d -> n_kv_heads*head_dim linear map (page "MoVA: routing
+ * the value vectors ...", section "So what does it cost?", which sets the
+ * 2.62M-parameter v_proj (2560 x 1024) against the routed experts; its
+ * section "The take" lists a decode kernel measured against a matched GQA
+ * baseline on the same hardware among the things wanted next):
+ *
+ *   out[t, h, j] = sum_c x[t, c] * w_v[h*head_dim + j, c]
+ *
+ *   x          bf16 [T, d]
+ *   w_v        bf16 [N, d]     nn.Linear layout, N = n_kv_heads*head_dim
+ *   out        bf16 [T, n_kv_heads, head_dim]
+ *   workspace  device scratch of at least mova_dense_workspace_bytes(...)
+ *              bytes, 256-byte aligned (may be NULL when that is 0).
+ *
+ * Products accumulate in fp32 and each output is rounded once to bf16
+ * (nearest even).  Up to 256 tokens the weight is split over d among many
+ * workgroups (fp32 partials in the workspace, added in a fixed order);
+ * larger T runs the tiled MFMA GEMM.  Results are bitwise reproducible for
+ * identical inputs.  Errors as for mova_value_forward.
+ */
+int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv_heads,
+                          int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * Stage timing (profiling aid).  While enabled, each mova_value_forward call
  * records a HIP event pair on the call's stream around each stage selected
  * by `stage_mask` (bit s = stage s), for up to `capacity` calls.  Stages:
  * 0 router, 1 dispatch, 2 expert projection (grouped GEMM or decode stream),
- * 3 combine.
+ * 3 combine; 4 is the whole of a mova_dense_value_proj call.
  *
  * mova_timing_enable(capacity, stage_mask) starts a new collection
  * (capacity <= 0 or stage_mask == 0 turns timing off); it creates host-side

@@ -18,7 +18,7 @@ from .build import LIBPATH
 _LIB = None
 
 MOVA_OK = 0
-STAGES = ("router", "dispatch", "experts", "combine")
+STAGES = ("router", "dispatch", "experts", "combine", "dense")
 
 
 class MovaError(RuntimeError):
@@ -47,6 +47,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mova_route.argtypes = [vp, vp, vp, i, i, i, i, f, vp, vp, vp]
     lib.mova_value_forward.restype = i
     lib.mova_value_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, vp, vp, sz, vp]
+    lib.mova_dense_workspace_bytes.restype = sz
+    lib.mova_dense_workspace_bytes.argtypes = [i, i, i, i]
+    lib.mova_dense_value_proj.restype = i
+    lib.mova_dense_value_proj.argtypes = [vp, vp, i, i, i, i, vp, vp, sz, vp]
     lib.mova_timing_enable.restype = i
     lib.mova_timing_enable.argtypes = [i, ctypes.c_uint]
     lib.mova_timing_read.restype = i
@@ -156,6 +160,43 @@ def value_forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[to
                                 workspace.numel(), _stream(dev))
     if rc != MOVA_OK:
         raise MovaError(rc, "mova_value_forward")
+    return out
+
+
+def dense_workspace_bytes(T: int, d: int, n_kv_heads: int, head_dim: int) -> int:
+    n = load_library().mova_dense_workspace_bytes(T, d, n_kv_heads, head_dim)
+    if n == ctypes.c_size_t(-1).value:
+        raise MovaError(-2, "mova_dense_workspace_bytes")
+    return n
+
+
+def dense_value_proj(x: torch.Tensor, w_v: torch.Tensor, n_kv_heads: Optional[int] = None,
+                     head_dim: int = 128, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mova_dense_value_proj: the plain value projection x w_v^T as bf16
+    [T, n_kv_heads, head_dim] (w_v is bf16 [n_kv_heads * head_dim, d])."""
+    lib = load_library()
+    T, d = x.shape
+    N, d2 = w_v.shape
+    if d2 != d:
+        raise ValueError("w_v's last dim must equal x's width")
+    if n_kv_heads is None:
+        n_kv_heads = N // head_dim
+    if n_kv_heads * head_dim != N:
+        raise ValueError("n_kv_heads * head_dim must equal w_v's row count")
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(w_v, "w_v", torch.bfloat16, (N, d), dev)
+    if out is None:
+        out = torch.empty(T, n_kv_heads, head_dim, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, n_kv_heads, head_dim), dev)
+    nbytes = dense_workspace_bytes(T, d, n_kv_heads, head_dim)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = lib.mova_dense_value_proj(_ptr(x), _ptr(w_v), T, d, n_kv_heads, head_dim, _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_dense_value_proj")
     return out
 
 

@@ -48,13 +48,31 @@ struct GemmArgs {
   const float* topk_w;     // [T * k]
   const int32_t* expert_off;
   const int32_t* tile_base;
-  f16_t* partial;          // [T * k, N]
+  f16_t* partial;          // [T * k, N] (grouped mode)
+  __bf16* out;             // [T, N] (dense mode)
   int T, d, N, E, k;
 };
 int gemm_block_m();
 // Upper bound on M-tiles for any routing of T tokens.
 int gemm_max_mtiles(int T, int k, int E);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+// Dense mode of the tiled GEMM: out = x W^T over T rows and one [N, d] weight
+// (x, W, out, T, d, N are read; the routing fields are ignored).
+int dense_gemm_block_m(int T, int N);
+hipError_t launch_dense_gemm(const GemmArgs& a, hipStream_t stream);
+
+struct DenseArgs {
+  const __bf16* x;  // [T, d]
+  const __bf16* W;  // [N, d]
+  float* part;      // [dense_skinny_splits(d), T, N] fp32 scratch
+  __bf16* out;      // [T, N]
+  int T, d, N;
+};
+// The split-k dense kernel handles at most this many tokens per call.
+constexpr int kDenseSkinnyMaxT = 256;
+int dense_skinny_splits(int d);
+size_t dense_skinny_partial_floats(int T, int d, int N);
+hipError_t launch_dense_skinny(const DenseArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
   const __bf16* x;

@@ -16,7 +16,7 @@ namespace {
 
 using namespace mova;
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 constexpr int kMaxT = 1 << 24;
 // Token counts up to this take the weight-streaming decode path by default
 // (measured faster than the grouped path for every T up to its limit).
@@ -81,14 +81,32 @@ Layout layout(int T, int E, int k, int N) {
   return L;
 }
 
+// Dense projection: the split-k kernel (with its fp32 partials in the
+// workspace) up to kDenseSkinnyMaxT tokens, the tiled GEMM above.
+enum class DensePath { Skinny, Tiled };
+
+DensePath choose_dense_path(int T) {
+  const char* force = getenv("MOVA_DENSE_PATH");
+  const bool skinny_ok = T <= kDenseSkinnyMaxT;
+  if (force != nullptr) {
+    if (strcmp(force, "skinny") == 0 && skinny_ok) return DensePath::Skinny;
+    if (strcmp(force, "tiled") == 0) return DensePath::Tiled;
+  }
+  return skinny_ok ? DensePath::Skinny : DensePath::Tiled;
+}
+
+size_t dense_workspace(int T, int d, int N) {
+  return T <= kDenseSkinnyMaxT ? align256(dense_skinny_partial_floats(T, d, N) * 4) : 0;
+}
+
 // ---- stage timing -------------------------------------------------------
-constexpr int kStages = 4;
+constexpr int kStages = 5;
 struct Timing {
   std::mutex mu;
   int capacity = 0;
   unsigned mask = 0;
   std::vector<hipEvent_t> ev[kStages];  // pairs: start at 2i, stop at 2i+1
-  int used[kStages] = {0, 0, 0, 0};
+  int used[kStages] = {0, 0, 0, 0, 0};
 } g_timing;
 
 struct StageScope {
@@ -219,7 +237,7 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
     }
     if (err != hipSuccess) return MOVA_ERR_HIP;
     StageScope sc(2, stream);
-    GemmArgs ga{xb, wb, perm, w, eoff, tbase, partial, T, d, N, E, k};
+    GemmArgs ga{xb, wb, perm, w, eoff, tbase, partial, nullptr, T, d, N, E, k};
     err = launch_grouped_gemm(ga, stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
@@ -227,6 +245,41 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
     StageScope sc(3, stream);
     CombineArgs ca{partial, (__bf16*)out, T, N, k};
     err = launch_combine(ca, stream);
+  }
+  return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+}
+
+size_t mova_dense_workspace_bytes(int T, int d, int n_kv_heads, int head_dim) {
+  if (T < 0 || d <= 0 || T > kMaxT || d % 64 != 0) return (size_t)-1;
+  if (check_heads(n_kv_heads, head_dim) != MOVA_OK) return (size_t)-1;
+  if (T == 0) return 0;
+  return dense_workspace(T, d, n_kv_heads * head_dim);
+}
+
+int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv_heads,
+                          int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (T < 0 || d <= 0) return MOVA_ERR_INVALID_ARG;
+  if (T > kMaxT || d % 64 != 0) return MOVA_ERR_UNSUPPORTED;
+  int rc = check_heads(n_kv_heads, head_dim);
+  if (rc != MOVA_OK) return rc;
+  if (T == 0) return MOVA_OK;
+  if (x == nullptr || w_v == nullptr || out == nullptr) return MOVA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_v) || !aligned16(out)) return MOVA_ERR_INVALID_ARG;
+  const int N = n_kv_heads * head_dim;
+  const DensePath path = choose_dense_path(T);
+  hipError_t err;
+  if (path == DensePath::Skinny) {
+    if (workspace == nullptr || workspace_bytes < dense_workspace(T, d, N)) return MOVA_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return MOVA_ERR_INVALID_ARG;
+    StageScope sc(4, stream);
+    DenseArgs da{(const __bf16*)x, (const __bf16*)w_v, (float*)workspace, (__bf16*)out, T, d, N};
+    err = launch_dense_skinny(da, stream);
+  } else {
+    StageScope sc(4, stream);
+    GemmArgs ga{(const __bf16*)x, (const __bf16*)w_v, nullptr, nullptr, nullptr, nullptr,
+                nullptr, (__bf16*)out, T, d, N, 1, 1};
+    err = launch_dense_gemm(ga, stream);
   }
   return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }

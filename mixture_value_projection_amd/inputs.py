@@ -16,9 +16,10 @@ seed names the same tensors on every machine:
   argument of N is the standard deviation;
 * router bias ~ U(-0.01, 0.01), zero, or a Zipf-shaped bias (see
   ``zipf_bias``);
-* tensor order is fixed (x, router W, router bias, expert W) and each tensor
-  has its own sub-seed (seed + 0 .. seed + 3); layer ``l`` of a multi-layer
-  workload adds ``100 * l`` to the weight sub-seeds;
+* tensor order is fixed (x, router W, router bias, expert W, and the dense
+  v_proj weight of the matched baseline) and each tensor has its own sub-seed
+  (seed + 0 .. seed + 4); layer ``l`` of a multi-layer workload adds
+  ``100 * l`` to the weight sub-seeds;
 * floating values are drawn in fp32 and rounded to bf16 (round to nearest
   even) unless the workload is fp32.
 """
@@ -42,6 +43,7 @@ __all__ = [
     "make_router",
     "make_experts",
     "make_weights",
+    "make_dense_vproj",
     "make_workload",
 ]
 
@@ -171,6 +173,16 @@ def make_experts(shape: LayerShape, seed: int, dtype: torch.dtype = torch.bfloat
     std = 1.0 / math.sqrt(shape.d)
     g = _gen(seed + 100 * layer + 3)
     return _round(torch.randn(shape.E, shape.N, shape.d, generator=g) * std, dtype)
+
+
+def make_dense_vproj(shape: LayerShape, seed: int, dtype: torch.dtype = torch.bfloat16,
+                     layer: int = 0) -> torch.Tensor:
+    """Plain value-projection weight [N, d] ~ N(0, 1/sqrt(d)) of a dense layer
+    (nn.Linear layout, bias-free), the matched baseline of the experts; its
+    own sub-seed is seed + 100 * layer + 4."""
+    std = 1.0 / math.sqrt(shape.d)
+    g = _gen(seed + 100 * layer + 4)
+    return _round(torch.randn(shape.N, shape.d, generator=g) * std, dtype)
 
 
 def make_weights(shape: LayerShape, seed: int, dtype: torch.dtype = torch.bfloat16,

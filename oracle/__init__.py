@@ -10,8 +10,9 @@ Parity status per function (details in the module docstring of
 ``oracle.mova_oracle``):
 
 * ``router_logits``, ``sigmoid``, ``route`` (except the bias role and the
-  router's reduction order), ``combine_experts``, ``value_forward``: pinned
-  by the tests in ``tests/test_oracle_pins.py``;
+  router's reduction order), ``combine_experts``, ``value_forward`` and
+  ``dense_value_proj`` (the matched dense baseline): pinned by the tests in
+  ``tests/test_oracle_pins.py``;
 * the role of the router bias (added to the scores for selection only) and
   the router's summation order: parity unpinned -- no page prints a value
   that fixes them; they are documented readings.

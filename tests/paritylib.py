@@ -11,6 +11,13 @@ weights sum to the scale within W_TOL.
 
 Outputs (bf16): max |gpu - oracle| <= MAX_ABS and
 ||gpu - oracle||_2 / ||oracle||_2 <= REL_L2 over all compared elements.
+
+Dense value projection (one fp32 sum per output, rounded once to bf16): on
+top of the two output rules, every element is within half a bf16 step of the
+oracle (|gpu - oracle| <= 2^-8 |oracle| + DENSE_ATOL, DENSE_ATOL covering the
+fp32 accumulation), and at least DENSE_MATCH of the elements equal the
+oracle's value rounded to bf16 (they differ only where the fp32 sum lands on
+the other side of a rounding midpoint).
 """
 from __future__ import annotations
 
@@ -26,6 +33,8 @@ MARGIN = 1e-4
 W_TOL = 1e-4
 MAX_ABS = 2e-2
 REL_L2 = 5e-3
+DENSE_ATOL = 1e-3
+DENSE_MATCH = 0.99
 
 
 @dataclasses.dataclass
@@ -120,4 +129,19 @@ def full_check(gpu_inputs: dict, k: int, scale: float, H: int, D: int, out, idx,
     g = out.reshape(out.shape[0], -1)[torch.as_tensor(rows, device=out.device)]
     stats = check_output(g, ref_out, what)
     stats.update(near_ties=rc.near_ties, differing_sets=rc.differing_sets)
+    return stats
+
+
+def check_dense_output(gpu_out, ref_out, what: str = "") -> dict:
+    """The dense projection's rules (module docstring) on [rows, N] outputs."""
+    stats = check_output(gpu_out, ref_out, what)
+    g = gpu_out.float().cpu().double().numpy().reshape(ref_out.shape[0], -1)
+    r = np.asarray(ref_out, dtype=np.float64).reshape(ref_out.shape[0], -1)
+    excess = np.abs(g - r) - (2.0 ** -8) * np.abs(r)
+    worst = float(excess.max()) if excess.size else 0.0
+    assert worst <= DENSE_ATOL, f"{what}: an element is {worst:.3g} beyond half a bf16 step"
+    rb = torch.from_numpy(r).to(torch.bfloat16).double().numpy()
+    match = float((g == rb).mean()) if g.size else 1.0
+    assert match >= DENSE_MATCH, f"{what}: only {match:.4f} of elements equal bf16(oracle)"
+    stats.update(bf16_match=match)
     return stats

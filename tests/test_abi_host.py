@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mova_route", "mova_value_forward", "mova_workspace_bytes", "mova_status_str",
-              "mova_version", "mova_timing_enable", "mova_timing_read"):
+              "mova_version", "mova_timing_enable", "mova_timing_read",
+              "mova_dense_value_proj", "mova_dense_workspace_bytes"):
         assert n in names
 
 
@@ -118,11 +119,46 @@ def test_route_empty_is_noop(lib):
     assert rte(lib, T=0, x=None, idx=None, w=None) == OK
 
 
+def test_dense_workspace_bytes(lib):
+    assert binding.dense_workspace_bytes(0, 2560, 8, 128) == 0
+    for T in (1, 64, 256):
+        n = binding.dense_workspace_bytes(T, 2560, 8, 128)
+        assert n % 256 == 0 and n >= T * 1024 * 4   # at least one fp32 partial plane
+    assert binding.dense_workspace_bytes(257, 2560, 8, 128) == 0   # tiled GEMM: no workspace
+    bad = ctypes.c_size_t(-1).value
+    assert lib.mova_dense_workspace_bytes(16, 2500, 8, 128) == bad    # d % 64
+    assert lib.mova_dense_workspace_bytes(16, 2560, 3, 20) == bad     # N % 64
+    assert lib.mova_dense_workspace_bytes(-1, 2560, 8, 128) == bad
+
+
+def dense(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, T=16, d=256, H=2, D=32, out=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mova_dense_value_proj(a["x"], a["w"], a["T"], a["d"], a["H"], a["D"], a["out"],
+                                     a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), INVALID), (dict(d=0), INVALID), (dict(H=0), INVALID), (dict(d=100), UNSUPPORTED),
+    (dict(H=3, D=20), UNSUPPORTED), (dict(T=(1 << 24) + 1), UNSUPPORTED),
+    (dict(H=129, D=128), UNSUPPORTED), (dict(x=None), INVALID), (dict(w=None), INVALID),
+    (dict(out=None), INVALID), (dict(x=FAKE + 2), INVALID), (dict(w=FAKE + 8), INVALID),
+    (dict(out=FAKE + 4), INVALID), (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE),
+    (dict(ws=FAKE + 16), INVALID),
+])
+def test_dense_rejects(lib, kw, rc):
+    assert dense(lib, **kw) == rc
+
+
+def test_dense_empty_is_noop(lib):
+    assert dense(lib, T=0, x=None, out=None, ws=None, wsb=0) == OK
+
+
 def test_timing_read_without_records(lib):
-    tot = (ctypes.c_double * 4)()
-    cnt = (ctypes.c_int * 4)()
-    assert lib.mova_timing_read(4, tot, cnt) == OK
-    assert list(cnt) == [0, 0, 0, 0]
+    tot = (ctypes.c_double * 5)()
+    cnt = (ctypes.c_int * 5)()
+    assert lib.mova_timing_read(5, tot, cnt) == OK
+    assert list(cnt) == [0, 0, 0, 0, 0]
     assert lib.mova_timing_read(-1, tot, cnt) == INVALID
 
 

@@ -257,6 +257,45 @@ def test_page_work_counts():
     assert accounting.flops_per_token(2560, 64, 4, 1024) == 21_299_200
 
 
+# ------------------------------------------- dense v_proj (matched baseline)
+
+def test_dense_vproj_hand_example():
+    """Worked by hand: rows of w_v are the output units' weight vectors
+    (nn.Linear layout), out[t, n] = sum_c x[t, c] w_v[n, c]."""
+    x = [[1.0, 2.0], [3.0, 4.0]]
+    w_v = [[1.0, 0.0], [1.0, 1.0], [0.0, -1.0]]
+    assert oracle.dense_value_proj(x, w_v).tolist() == [[1.0, 3.0, -2.0], [3.0, 7.0, -4.0]]
+
+
+def test_dense_vproj_brute_force_loops():
+    """Pure-Python triple loop on a tiny non-square case."""
+    rng = np.random.default_rng(5)
+    T, d, N = 3, 7, 5
+    x = rng.standard_normal((T, d))
+    w = rng.standard_normal((N, d))
+    ref = [[math.fsum(x[t, c] * w[n, c] for c in range(d)) for n in range(N)] for t in range(T)]
+    np.testing.assert_allclose(oracle.dense_value_proj(x, w), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_dense_vproj_selector_weights():
+    """A weight whose rows are unit vectors picks (and permutes) x's columns."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 8))
+    perm = [5, 0, 7, 2]
+    w = np.zeros((4, 8))
+    w[np.arange(4), perm] = 1.0
+    assert np.array_equal(oracle.dense_value_proj(x, w), x[:, perm])
+
+
+def test_dense_vproj_accepts_torch_bf16():
+    """bf16 tensors are widened exactly (every bf16 value is an fp64 value)."""
+    x = inputs.make_tokens(3, 64, 9)
+    w = inputs.make_dense_vproj(inputs.LayerShape(T=3, d=64, E=1, k=1, n_kv_heads=1,
+                                                  head_dim=64), 9)
+    ref = x.double().numpy() @ w.double().numpy().T
+    assert np.array_equal(oracle.dense_value_proj(x, w), ref)
+
+
 def test_skewed_workload_load_ratio():
     """The skewed workload's bias gives max / mean expert load of 10 (+-5%)."""
     w = inputs.WORKLOADS["skewed"]
