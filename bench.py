@@ -126,6 +126,41 @@ def run_single_layer(name, steps, warmup, copies):
                 touched=touched, max_load=int(counts.max()), mean_load=float(counts.mean()))
 
 
+def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
+    """The decode step with its value rows stored straight into a paged pool
+    (num_blocks x block_size slots of [8, 128] bf16, 128 MB) at distinct
+    random slots, no contiguous output."""
+    w = inputs.WORKLOADS["decode"]
+    sh = w.shape
+    x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
+    cps = make_copies(sh, w.seed, w.dtype, w.bias, copies)
+    pool = torch.zeros(num_blocks, block_size, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16,
+                       device=DEV)
+    g = torch.Generator().manual_seed(5)
+    slots = torch.randperm(num_blocks * block_size, generator=g)[:sh.T].to(DEV)
+    ws = torch.empty(binding.workspace_bytes(sh.T, sh.d, sh.E, sh.k, sh.n_kv_heads, sh.head_dim),
+                     dtype=torch.uint8, device=DEV)
+
+    def mk(c):
+        return lambda: binding.value_forward_paged(x, c["router_w"], c["router_b"], c["expert_w"],
+                                                   sh.k, sh.scale, pool, slots, workspace=ws)
+    calls = [mk(c) for c in cps]
+    gsecs, gcalls = graph_time(calls, steps, warmup)
+    # Unfused reference: the plain forward, then a separate scatter of the
+    # contiguous rows into the pool (torch index_copy_).
+    out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+    flat = pool.view(num_blocks * block_size, sh.N)
+
+    def mk2(c):
+        def f():
+            binding.value_forward(x, c["router_w"], c["router_b"], c["expert_w"], sh.k, sh.scale,
+                                  sh.n_kv_heads, sh.head_dim, out=out, workspace=ws)
+            flat.index_copy_(0, slots, out.view(sh.T, sh.N))
+        return f
+    usecs, ucalls = graph_time([mk2(c) for c in cps], steps, warmup)
+    return 1e6 * gsecs / gcalls, 1e6 * usecs / ucalls
+
+
 def run_chunked(steps, warmup):
     """One step = the whole 65536-token stream through 4 layers (32 calls)."""
     w = inputs.WORKLOADS["chunked"]
@@ -373,6 +408,13 @@ def main():
             gqa.append(dense_line(name, rr, mova_us[name]))
             torch.cuda.empty_cache()
         line["gqa_baseline"] = gqa
+        log("paged decode ...")
+        pus, uus = run_paged_decode(args.steps, args.warmup, args.copies)
+        line["paged_decode"] = {"us_per_step": pus, "plain_us_per_step": 1e6 * step_s,
+                                "unfused_us_per_step": uus,
+                                "tokens_per_s": sh.T / (pus * 1e-6),
+                                "pool": "4096 blocks x 16 slots x [8, 128] bf16, distinct random "
+                                        "slots, no contiguous output"}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline()

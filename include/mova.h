@@ -113,6 +113,40 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The same value projection with the result stored straight into a paged
+ * value cache: the routed vector of each token is what the cache keeps
+ * (page "IFM K2 Horizon Deep Dive: Inside Mixture-of-Value Attention (MoVA)
+ * ...", section "The Two Architectural Caching Strategies for MoVA", Option
+ * A, the post-routing projected value cache in the ordinary paged-attention
+ * pools; page "MoVA: routing the value vectors ...", section "Where the
+ * routing happens", hands that [n_kv_heads, head_dim] vector to the cache
+ * update).  The k-way combine writes each row once to the pool, and to `out`
+ * as well when `out` is not NULL, so the cache store costs no extra pass.
+ *
+ *   v_cache      bf16  [num_blocks, block_size, n_kv_heads, head_dim]
+ *                the pool; slot s is row s % block_size of block
+ *                s / block_size, i.e. the s-th [n_kv_heads, head_dim] row
+ *   slot_mapping int64 [T]  slot of each token; a slot outside
+ *                [0, num_blocks * block_size) -- e.g. -1 for padding --
+ *                stores nothing.  8-byte aligned.
+ *   out          bf16  [T, n_kv_heads, head_dim] or NULL
+ *   other arguments, workspace and numerics as for mova_value_forward (the
+ *   pool rows get exactly the bits `out` gets).
+ *
+ * Rows of the pool that no token's slot names are left untouched.  Two
+ * tokens naming the same slot race: that row's contents are unspecified.
+ * Returns MOVA_ERR_INVALID_ARG for num_blocks < 0, block_size <= 0, a NULL
+ * or misaligned v_cache or slot_mapping (T > 0), MOVA_ERR_UNSUPPORTED for a
+ * pool of more than 2^40 slots; otherwise as mova_value_forward.
+ */
+int mova_value_forward_paged(const void* x, const void* router_w, const float* router_b,
+                             const void* expert_w, int T, int d, int E, int k, float scale,
+                             int n_kv_heads, int head_dim, void* v_cache, int num_blocks,
+                             int block_size, const int64_t* slot_mapping, void* out,
+                             int32_t* topk_idx_out, float* topk_w_out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Bytes of device workspace mova_dense_value_proj needs for these sizes: 0
  * when T == 0 or T > 256, (size_t)-1 outside the supported domain (that of
  * mova_value_forward without the router's E and k).

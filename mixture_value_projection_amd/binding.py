@@ -47,6 +47,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mova_route.argtypes = [vp, vp, vp, i, i, i, i, f, vp, vp, vp]
     lib.mova_value_forward.restype = i
     lib.mova_value_forward.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, vp, vp, sz, vp]
+    lib.mova_value_forward_paged.restype = i
+    lib.mova_value_forward_paged.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, i, i, vp, vp,
+                                             vp, vp, vp, sz, vp]
     lib.mova_dense_workspace_bytes.restype = sz
     lib.mova_dense_workspace_bytes.argtypes = [i, i, i, i]
     lib.mova_dense_value_proj.restype = i
@@ -160,6 +163,52 @@ def value_forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[to
                                 workspace.numel(), _stream(dev))
     if rc != MOVA_OK:
         raise MovaError(rc, "mova_value_forward")
+    return out
+
+
+def value_forward_paged(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
+                        expert_w: torch.Tensor, k: int, scale: float, v_cache: torch.Tensor,
+                        slot_mapping: torch.Tensor, out: Optional[torch.Tensor] = None,
+                        topk_idx: Optional[torch.Tensor] = None,
+                        topk_w: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """mova_value_forward_paged: stores each token's value vector in
+    ``v_cache`` (bf16 [num_blocks, block_size, n_kv_heads, head_dim]) at
+    ``slot_mapping[t]`` (int64 [T]; slots outside the pool store nothing) and,
+    if ``out`` is given, in ``out`` too.  Returns ``out``."""
+    lib = load_library()
+    T, d = x.shape
+    E, N, d2 = expert_w.shape
+    if d2 != d:
+        raise ValueError("expert_w's last dim must equal x's width")
+    if v_cache.dim() != 4:
+        raise ValueError("v_cache must be [num_blocks, block_size, n_kv_heads, head_dim]")
+    nb, bs, H, D = v_cache.shape
+    if H * D != N:
+        raise ValueError("v_cache's n_kv_heads * head_dim must equal the expert width")
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(router_w, "router_w", torch.bfloat16, (E, d), dev)
+    if router_b is not None:
+        _check(router_b, "router_b", torch.float32, (E,), dev)
+    _check(expert_w, "expert_w", torch.bfloat16, (E, N, d), dev)
+    _check(v_cache, "v_cache", torch.bfloat16, (nb, bs, H, D), dev)
+    _check(slot_mapping, "slot_mapping", torch.int64, (T,), dev)
+    if out is not None:
+        _check(out, "out", torch.bfloat16, (T, H, D), dev)
+    if topk_idx is not None:
+        _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    if topk_w is not None:
+        _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    nbytes = workspace_bytes(T, d, E, k, H, D)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = lib.mova_value_forward_paged(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_w),
+                                      T, d, E, k, float(scale), H, D, _ptr(v_cache), nb, bs,
+                                      _ptr(slot_mapping), _ptr(out), _ptr(topk_idx), _ptr(topk_w),
+                                      _ptr(workspace), workspace.numel(), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_value_forward_paged")
     return out
 
 

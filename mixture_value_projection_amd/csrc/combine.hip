@@ -4,6 +4,13 @@
 // value tensor with column n = h * head_dim + j (page "MoVA: routing the
 // value vectors ...", section "Where the routing happens": the mixture is
 // summed per token and viewed as heads of 128).
+//
+// Paged variant: the same row is also (or only) stored at row slot[t] of a
+// paged value pool [num_blocks, block_size, n_kv_heads, head_dim], whose rows
+// are contiguous N-element vectors, so slot s is simply row s (page "IFM K2
+// Horizon Deep Dive ...", section "The Two Architectural Caching Strategies
+// for MoVA", Option A: the routed vector is kept in the ordinary paged
+// pools).  Slots outside [0, num_slots) store nothing.
 #include <algorithm>
 
 #include "common.h"
@@ -13,8 +20,12 @@ namespace mova {
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
+template <bool kPaged>
 __global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ partial,
-                                                      bf16_t* __restrict__ out, int T, int N, int k) {
+                                                      bf16_t* __restrict__ out, int T, int N, int k,
+                                                      const int64_t* __restrict__ slot,
+                                                      long long num_slots,
+                                                      bf16_t* __restrict__ cache) {
   const int vec_per_row = N / 8;
   const long long total = (long long)T * vec_per_row;
   for (long long v = blockIdx.x * 256ll + threadIdx.x; v < total; v += (long long)gridDim.x * 256) {
@@ -36,14 +47,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       packed[i] = (uint32_t)f32_to_bf16_bits(s[2 * i]) | ((uint32_t)f32_to_bf16_bits(s[2 * i + 1]) << 16);
-    store16(out + (size_t)t * N + c, packed);
+    if (!kPaged) {
+      store16(out + (size_t)t * N + c, packed);
+    } else {
+      if (out != nullptr) store16(out + (size_t)t * N + c, packed);
+      const long long sl = slot[t];
+      if (sl >= 0 && sl < num_slots) store16(cache + (size_t)sl * N + c, packed);
+    }
   }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const long long total = (long long)a.T * (a.N / 8);
   const long long blocks = std::min<long long>((total + 255) / 256, 256ll * 16);
-  combine_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k);
+  if (a.cache == nullptr)
+    combine_kernel<false><<<dim3((unsigned)blocks), 256, 0, stream>>>(a.partial, a.out, a.T, a.N,
+                                                                      a.k, nullptr, 0, nullptr);
+  else
+    combine_kernel<true><<<dim3((unsigned)blocks), 256, 0, stream>>>(
+        a.partial, a.out, a.T, a.N, a.k, a.slot, a.num_slots, a.cache);
   return hipGetLastError();
 }
 

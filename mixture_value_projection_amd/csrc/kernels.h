@@ -88,8 +88,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 struct CombineArgs {
   const f16_t* partial;  // [T * k, N]
-  __bf16* out;           // [T, N]
+  __bf16* out;           // [T, N]; may be null when cache is set
   int T, N, k;
+  // Paged store (cache null = none): row t also goes to cache row slot[t]
+  // when 0 <= slot[t] < num_slots.
+  const int64_t* slot = nullptr;
+  long long num_slots = 0;
+  __bf16* cache = nullptr;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

@@ -81,6 +81,16 @@ Layout layout(int T, int E, int k, int N) {
   return L;
 }
 
+// Paged store of the value rows (mova_value_forward_paged).
+struct PagedStore {
+  void* cache;
+  const int64_t* slot;
+  int num_blocks, block_size;
+};
+// Largest pool, in slots, that the paged entry point accepts (a row index
+// times N stays far inside 64-bit offsets).
+constexpr long long kMaxSlots = 1ll << 40;
+
 // Dense projection: the split-k kernel (with its fp32 partials in the
 // workspace) up to kDenseSkinnyMaxT tokens, the tiled GEMM above.
 enum class DensePath { Skinny, Tiled };
@@ -180,18 +190,27 @@ int mova_route(const void* x, const void* router_w, const float* router_b, int T
   return launch_router_tile(ra, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }
 
-int mova_value_forward(const void* x, const void* router_w, const float* router_b,
-                       const void* expert_w, int T, int d, int E, int k, float scale,
-                       int n_kv_heads, int head_dim, void* out, int32_t* topk_idx_out,
-                       float* topk_w_out, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+// Shared body of mova_value_forward and mova_value_forward_paged.  `pg` set:
+// the combine also stores each row at its slot of the paged pool, and `out`
+// may be null.
+static int value_forward_impl(const void* x, const void* router_w, const float* router_b,
+                              const void* expert_w, int T, int d, int E, int k, float scale,
+                              int n_kv_heads, int head_dim, void* out, const PagedStore* pg,
+                              int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
   int rc = check_shape(T, d, E, k);
   if (rc != MOVA_OK) return rc;
   rc = check_heads(n_kv_heads, head_dim);
   if (rc != MOVA_OK) return rc;
   if (!isfinite(scale)) return MOVA_ERR_UNSUPPORTED;
+  if (pg != nullptr && (pg->num_blocks < 0 || pg->block_size <= 0)) return MOVA_ERR_INVALID_ARG;
+  if (pg != nullptr && (long long)pg->num_blocks * pg->block_size > kMaxSlots)
+    return MOVA_ERR_UNSUPPORTED;
   if (T == 0) return MOVA_OK;
-  if (x == nullptr || router_w == nullptr || expert_w == nullptr || out == nullptr)
+  if (x == nullptr || router_w == nullptr || expert_w == nullptr || (out == nullptr && pg == nullptr))
+    return MOVA_ERR_INVALID_ARG;
+  if (pg != nullptr && (pg->cache == nullptr || pg->slot == nullptr)) return MOVA_ERR_INVALID_ARG;
+  if (pg != nullptr && (!aligned16(pg->cache) || ((uintptr_t)pg->slot & 7u) != 0))
     return MOVA_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(router_w) || !aligned16(router_b) || !aligned16(expert_w) ||
       !aligned16(out) || !aligned16(topk_idx_out) || !aligned16(topk_w_out))
@@ -244,9 +263,36 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
   {
     StageScope sc(3, stream);
     CombineArgs ca{partial, (__bf16*)out, T, N, k};
+    if (pg != nullptr) {
+      ca.slot = pg->slot;
+      ca.num_slots = (long long)pg->num_blocks * pg->block_size;
+      ca.cache = (__bf16*)pg->cache;
+    }
     err = launch_combine(ca, stream);
   }
   return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+}
+
+int mova_value_forward(const void* x, const void* router_w, const float* router_b,
+                       const void* expert_w, int T, int d, int E, int k, float scale,
+                       int n_kv_heads, int head_dim, void* out, int32_t* topk_idx_out,
+                       float* topk_w_out, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return value_forward_impl(x, router_w, router_b, expert_w, T, d, E, k, scale, n_kv_heads,
+                            head_dim, out, nullptr, topk_idx_out, topk_w_out, workspace,
+                            workspace_bytes, stream);
+}
+
+int mova_value_forward_paged(const void* x, const void* router_w, const float* router_b,
+                             const void* expert_w, int T, int d, int E, int k, float scale,
+                             int n_kv_heads, int head_dim, void* v_cache, int num_blocks,
+                             int block_size, const int64_t* slot_mapping, void* out,
+                             int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  const PagedStore pg{v_cache, slot_mapping, num_blocks, block_size};
+  return value_forward_impl(x, router_w, router_b, expert_w, T, d, E, k, scale, n_kv_heads,
+                            head_dim, out, &pg, topk_idx_out, topk_w_out, workspace,
+                            workspace_bytes, stream);
 }
 
 size_t mova_dense_workspace_bytes(int T, int d, int n_kv_heads, int head_dim) {

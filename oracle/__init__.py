@@ -11,7 +11,8 @@ Parity status per function (details in the module docstring of
 
 * ``router_logits``, ``sigmoid``, ``route`` (except the bias role and the
   router's reduction order), ``combine_experts``, ``value_forward`` and
-  ``dense_value_proj`` (the matched dense baseline): pinned by the tests in
+  ``dense_value_proj`` (the matched dense baseline) and
+  ``paged_value_write`` (the paged cache store): pinned by the tests in
   ``tests/test_oracle_pins.py``;
 * the role of the router bias (added to the scores for selection only) and
   the router's summation order: parity unpinned -- no page prints a value
@@ -22,6 +23,7 @@ from .mova_oracle import (  # noqa: F401
     Routing,
     combine_experts,
     dense_value_proj,
+    paged_value_write,
     route,
     router_logits,
     sigmoid,

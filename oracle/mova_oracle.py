@@ -173,3 +173,28 @@ def dense_value_proj(x, w_v) -> np.ndarray:
     """Plain GQA value projection V = x W_v^T (the dense layers' v_proj, section
     "So what does it cost?"), float64."""
     return _f64(x) @ _f64(w_v).T
+
+
+def paged_value_write(cache, values, slot_mapping) -> np.ndarray:
+    """Store each token's value vector in a paged pool (Option A of the page
+    "IFM K2 Horizon Deep Dive: Inside Mixture-of-Value Attention (MoVA) ...",
+    section "The Two Architectural Caching Strategies for MoVA": the routed
+    projection is computed per token and the resulting vector is kept in the
+    ordinary paged-attention memory pools; page 2's "Where the routing
+    happens" hands that [8, 128] vector to the cache update).
+
+    cache: [num_blocks, block_size, H, D]; values: [T, H, D]; slot_mapping:
+    [T] integers.  Slot s is row s % block_size of block s // block_size.
+    Reading (the pages do not fix the pool layout or padding): token-major
+    blocks as above, and a slot outside [0, num_blocks * block_size) -- a
+    negative padding slot in particular -- stores nothing.  Returns a new
+    float64 array; the input is not modified.
+    """
+    out = _f64(cache).copy()
+    vals = _f64(values)
+    nb, bs = out.shape[0], out.shape[1]
+    for t, s in enumerate(np.asarray(slot_mapping).tolist()):
+        s = int(s)
+        if 0 <= s < nb * bs:
+            out[s // bs, s % bs] = vals[t]
+    return out

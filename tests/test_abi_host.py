@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("mova_route", "mova_value_forward", "mova_workspace_bytes", "mova_status_str",
               "mova_version", "mova_timing_enable", "mova_timing_read",
-              "mova_dense_value_proj", "mova_dense_workspace_bytes"):
+              "mova_dense_value_proj", "mova_dense_workspace_bytes",
+              "mova_value_forward_paged"):
         assert n in names
 
 
@@ -117,6 +118,33 @@ def test_route_rejects(lib, kw, rc):
 
 def test_route_empty_is_noop(lib):
     assert rte(lib, T=0, x=None, idx=None, w=None) == OK
+
+
+def paged(lib, **kw):
+    a = dict(x=FAKE, rw=FAKE, rb=None, ew=FAKE, T=16, d=256, E=8, k=2, scale=2.5, H=2, D=32,
+             cache=FAKE, nb=4, bs=16, slot=FAKE + 8, out=None, idx=None, w=None, ws=FAKE,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mova_value_forward_paged(a["x"], a["rw"], a["rb"], a["ew"], a["T"], a["d"], a["E"],
+                                        a["k"], a["scale"], a["H"], a["D"], a["cache"], a["nb"],
+                                        a["bs"], a["slot"], a["out"], a["idx"], a["w"], a["ws"],
+                                        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), INVALID), (dict(E=65), UNSUPPORTED), (dict(d=100), UNSUPPORTED),
+    (dict(scale=float("nan")), UNSUPPORTED), (dict(nb=-1), INVALID), (dict(bs=0), INVALID),
+    (dict(nb=1 << 30, bs=1 << 12), UNSUPPORTED), (dict(cache=None), INVALID),
+    (dict(slot=None), INVALID), (dict(cache=FAKE + 8), INVALID), (dict(slot=FAKE + 4), INVALID),
+    (dict(out=FAKE + 2), INVALID), (dict(x=None), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(wsb=1024), WORKSPACE),
+])
+def test_paged_rejects(lib, kw, rc):
+    assert paged(lib, **kw) == rc
+
+
+def test_paged_empty_is_noop(lib):
+    assert paged(lib, T=0, x=None, cache=None, slot=None, ws=None, wsb=0) == OK
 
 
 def test_dense_workspace_bytes(lib):

@@ -296,6 +296,37 @@ def test_dense_vproj_accepts_torch_bf16():
     assert np.array_equal(oracle.dense_value_proj(x, w), ref)
 
 
+# ------------------------------------------------ paged value cache (Option A)
+
+def test_paged_write_hand_example():
+    """Worked by hand: 3 blocks of 2 slots, H = 1, D = 2.  Slot 3 is block 1
+    row 1, slot 0 is block 0 row 0; slot -1 (padding) and slot 6 (past the
+    pool) store nothing."""
+    cache = np.full((3, 2, 1, 2), 9.0)
+    values = np.array([[[1.0, 2.0]], [[3.0, 4.0]], [[5.0, 6.0]], [[7.0, 8.0]]])
+    got = oracle.paged_value_write(cache, values, [3, -1, 0, 6])
+    want = np.full((3, 2, 1, 2), 9.0)
+    want[1, 1, 0] = [1.0, 2.0]
+    want[0, 0, 0] = [5.0, 6.0]
+    assert np.array_equal(got, want)
+    assert (cache == 9.0).all()   # input untouched
+
+
+def test_paged_write_permutation_round_trip():
+    """Writing T tokens to a permutation of slots, then reading the pool back
+    through the same slots, returns the values; every other slot keeps its
+    sentinel."""
+    rng = np.random.default_rng(8)
+    nb, bs, H, D, T = 7, 4, 2, 3, 19
+    values = rng.standard_normal((T, H, D))
+    slots = rng.permutation(nb * bs)[:T]
+    got = oracle.paged_value_write(np.full((nb, bs, H, D), -7.0), values, slots)
+    flat = got.reshape(nb * bs, H, D)
+    assert np.array_equal(flat[slots], values)
+    rest = np.setdiff1d(np.arange(nb * bs), slots)
+    assert (flat[rest] == -7.0).all()
+
+
 def test_skewed_workload_load_ratio():
     """The skewed workload's bias gives max / mean expert load of 10 (+-5%)."""
     w = inputs.WORKLOADS["skewed"]
