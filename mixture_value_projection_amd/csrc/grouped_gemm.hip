@@ -16,48 +16,104 @@
 // epilogue stores z rounded once to bf16 (the dense layers' plain v_proj,
 // section "So what does it cost?").
 //
-// Block tile BM x BN (BM = 256 or 128, BN = 256), k steps of 64, 8 waves in a
-// 2 x 4 grid, each wave owning a BM/2 x 64 sub-tile (BM/32 x 4 MFMA 16x16x32
-// tiles).  Operand tiles go global -> LDS with direct (global_load_lds)
-// 16-byte loads, double buffered: the loads of step k+1 are in flight while
-// step k's MFMAs run, with one barrier per step.  A staged row holds 64 bf16
-// (128 B) whose 16-byte chunks sit at chunk ^ (row & 7), so the MFMA fragment
-// reads hit distinct banks; since a direct load writes 64 consecutive 16-byte
-// slots, the swizzle is applied when choosing which global chunk each lane
-// loads.
+// Block tile BM x BN (256 x 256, 128 x 256 or 128 x 128), k steps of 64, 8
+// waves in a 2 x 4 grid (or 4 waves in 2 x 2 for 128 x 128), each wave owning
+// a BM/2 x BN/4 (or BM/2 x BN/2) sub-tile of 16x16x32 MFMA tiles.  Operand
+// tiles go global -> LDS with direct (global_load_lds) 16-byte loads into a
+// ring of LDS stages: with 2 stages the loads of step k+1 are in flight while
+// step k's MFMAs run, one barrier per step; with 3 or 4 stages (128 x 128
+// only) the loads run 2 or 3 steps ahead, which pays when one workgroup per
+// CU has to keep the CU's loads in flight by itself.  A staged row holds 64
+// bf16 (128 B) whose 16-byte chunks sit at chunk ^ (row & 7), so the MFMA
+// fragment reads hit distinct banks; since a direct load writes 64
+// consecutive 16-byte slots, the swizzle is applied when choosing which
+// global chunk each lane loads.
 //
-// A tile with at most BM/2 valid rows runs its lower waves through a copy of
-// the k loop that only loads and synchronises (no MFMA work on empty rows).
+// Tile choice (measured on the decode, prefill, chunked and skewed shapes):
+// grouped mode takes 128 x 128 (2 stages, two workgroups per CU) while the
+// experts average at most 256 rows, else 256 x 256; dense mode takes 256 x
+// 256 once those tiles fill the 256 CUs, else 128 x 128 with 4 stages when
+// the grid is a single round of workgroups and 2 stages otherwise.
+//
+// A tile whose valid rows end in the upper half keeps its lower waves in the
+// k loop for the loads and barriers only (no MFMA work on empty rows).
 //
 // Work order: tile id -> (expert, n-tile, m-tile), m fastest, so tiles that
 // share an expert's weight slab are adjacent.  Workgroups are dealt round
 // robin over the 8 XCDs; block b runs tile (b % 8) * per_xcd + b / 8, giving
 // each XCD one contiguous run of tiles (and its L2 the weights they share).
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace mova {
 
-constexpr int kBMGrouped = 256;  // M tile of the grouped (routed) mode
-constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int kThreads = 512;
 constexpr int kRowBytes = BK * 2;  // 128 B per staged row
-constexpr int kTileB = BN * kRowBytes;  // 32 KB
 constexpr int kXcds = 8;
-constexpr int kLoadsB = BN * kRowBytes / 1024 / (kThreads / 64);  // 4 direct loads per wave
 
-template <int kBM>
+// kBM x kBN block tile over a kWM x kWN grid of waves, kS LDS stages.
+template <int kBM, int kBN, int kWM, int kWN, int kS>
 struct Tile {
-  static constexpr int kTileA = kBM * kRowBytes;                       // 32 or 16 KB
-  static constexpr int kStage = kTileA + kTileB;                       // 64 or 48 KB per buffer
-  static constexpr int kLoadsA = kBM * kRowBytes / 1024 / (kThreads / 64);  // 4 or 2
-  static constexpr int kMI = kBM / 32;                                 // MFMA row tiles per wave
+  static constexpr int kWaves = kWM * kWN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kTileA = kBM * kRowBytes;
+  static constexpr int kTileB = kBN * kRowBytes;
+  static constexpr int kStage = kTileA + kTileB;  // per buffer
+  static constexpr int kLoadsA = kBM * kRowBytes / 1024 / kWaves;  // 1 KB direct loads per wave
+  static constexpr int kLoadsB = kBN * kRowBytes / 1024 / kWaves;
+  static constexpr int kRowsW = kBM / kWM;  // rows per wave
+  static constexpr int kColsW = kBN / kWN;  // columns per wave
+  static constexpr int kMI = kRowsW / 16;   // MFMA row tiles per wave
+  static constexpr int kNJ = kColsW / 16;   // MFMA column tiles per wave
 };
+#define MOVA_TILE_PARAMS int kBM, int kBN, int kWM, int kWN, int kS
+#define MOVA_TILE_ARGS kBM, kBN, kWM, kWN, kS
 
-int gemm_block_m() { return kBMGrouped; }
+// s_waitcnt immediate: at most n vector-memory operations of this wave still
+// outstanding, and all of its LDS operations complete.
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-int gemm_max_mtiles(int T, int k, int E) { return (int)(((long long)T * k) / kBMGrouped) + E; }
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// waits for every outstanding direct-to-LDS load, which would drain the
+// multi-stage ring.  The caller waits on the counters it needs first; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Tile shapes a caller can force with MOVA_GEMM_TILE (tests, measurements).
+static bool forced_tile(GemmTile* t) {
+  const char* force = getenv("MOVA_GEMM_TILE");
+  if (force == nullptr) return false;
+  static const struct {
+    const char* name;
+    GemmTile tile;
+  } kTiles[] = {{"256x256", {256, 256, 8, 2}},   {"128x256", {128, 256, 8, 2}},
+                {"128x128", {128, 128, 8, 2}},   {"128x128s3", {128, 128, 8, 3}},
+                {"128x128s4", {128, 128, 8, 4}}, {"128x128w4", {128, 128, 4, 4}}};
+  for (const auto& c : kTiles)
+    if (strcmp(force, c.name) == 0) {
+      *t = c.tile;
+      return true;
+    }
+  return false;
+}
+
+GemmTile gemm_tile_grouped(int T, int k, int E) {
+  GemmTile t;
+  if (forced_tile(&t)) return t;
+  // 128 x 128 tiles (two workgroups per CU) while the experts average at most
+  // 256 rows, where 256-row tiles are mostly padding; 256 x 256 above.
+  if ((long long)T * k <= 256ll * E) return {128, 128, 8, 2};
+  return {256, 256, 8, 2};
+}
+
+int gemm_max_mtiles(int T, int k, int E, int bm) { return (int)(((long long)T * k) / bm) + E; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -65,64 +121,66 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ (row & 7)) << 4);
 }
 
-template <int kBM>
+template <MOVA_TILE_PARAMS>
 struct TileCtx {
-  const char* a_src[Tile<kBM>::kLoadsA];  // per lane: (gathered) x row + its chunk
-  const char* b_src[kLoadsB];             // per lane: weight row + its chunk
+  const char* a_src[Tile<MOVA_TILE_ARGS>::kLoadsA];  // per lane: (gathered) x row + its chunk
+  const char* b_src[Tile<MOVA_TILE_ARGS>::kLoadsB];  // per lane: weight row + its chunk
 };
 
 // Direct loads of one k step: A block j (rows 8j .. 8j+7) for j = wave * kLoadsA + i,
 // B block j for j = wave * kLoadsB + i.
-template <int kBM>
-__device__ __forceinline__ void issue_loads(const TileCtx<kBM>& c, char* stage, int wave,
+template <MOVA_TILE_PARAMS>
+__device__ __forceinline__ void issue_loads(const TileCtx<MOVA_TILE_ARGS>& c, char* stage, int wave,
                                             int k_byte) {
+  using TL = Tile<MOVA_TILE_ARGS>;
 #pragma unroll
-  for (int i = 0; i < Tile<kBM>::kLoadsA; ++i)
+  for (int i = 0; i < TL::kLoadsA; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(c.a_src[i] + k_byte),
-                                     (lds_void*)(stage + (wave * Tile<kBM>::kLoadsA + i) * 1024),
-                                     16, 0, 0);
+                                     (lds_void*)(stage + (wave * TL::kLoadsA + i) * 1024), 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < kLoadsB; ++i)
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(c.b_src[i] + k_byte),
-        (lds_void*)(stage + Tile<kBM>::kTileA + (wave * kLoadsB + i) * 1024), 16, 0, 0);
+  for (int i = 0; i < TL::kLoadsB; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(c.b_src[i] + k_byte),
+                                     (lds_void*)(stage + TL::kTileA + (wave * TL::kLoadsB + i) * 1024),
+                                     16, 0, 0);
 }
 
-// One k step (two 32-wide MFMA steps) of the wave's BM/2 x 64 sub-tile.
-template <int kBM>
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[Tile<kBM>::kMI][4], const char* stage,
-                                         int wm, int wn, int q, int r16) {
-  constexpr int MI = Tile<kBM>::kMI;
+// One k step (two 32-wide MFMA steps) of the wave's sub-tile.
+template <MOVA_TILE_PARAMS>
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[kBM / kWM / 16][kBN / kWN / 16],
+                                         const char* stage, int wm, int wn, int q, int r16) {
+  using TL = Tile<MOVA_TILE_ARGS>;
+  constexpr int MI = TL::kMI, NJ = TL::kNJ;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int chunk = ks * 4 + q;
-    Frag16 fa[MI], fb[4];
+    Frag16 fa[MI], fb[NJ];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[i].u = load16(stage + swz(wm * (kBM / 2) + i * 16 + r16, chunk));
+    for (int i = 0; i < MI; ++i) fa[i].u = load16(stage + swz(wm * TL::kRowsW + i * 16 + r16, chunk));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[j].u = load16(stage + Tile<kBM>::kTileA + swz(wn * 64 + j * 16 + r16, chunk));
+    for (int j = 0; j < NJ; ++j)
+      fb[j].u = load16(stage + TL::kTileA + swz(wn * TL::kColsW + j * 16 + r16, chunk));
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(fa[i].h, fb[j].h, acc[i][j]);
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(fa[i].h, fb[j].h, acc[i][j]);
   }
 }
 
 // kDense = false: grouped mode (perm, topk_w, expert_off, tile_base, partial).
 // kDense = true: dense mode over T token rows and one [N, d] weight (out).
-template <int kBM, bool kDense>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
+template <MOVA_TILE_PARAMS, bool kDense>
+__global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ perm, const float* __restrict__ topk_w,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_base,
     f16_t* __restrict__ partial, bf16_t* __restrict__ out, int T, int d, int N, int E, int k) {
-  using TL = Tile<kBM>;
+  using TL = Tile<MOVA_TILE_ARGS>;
+  constexpr int WN = TL::kColsW;  // columns per wave
   extern __shared__ __attribute__((aligned(1024))) char smem[];  // 2 stages
   __shared__ int tile_pair[kDense ? 1 : kBM];
   __shared__ float tile_w[kDense ? 1 : kBM];
 
-  const int NT = ceil_div(N, BN);
+  const int NT = ceil_div(N, kBN);
   const int MTd = kDense ? ceil_div(T, kBM) : 0;
   const int total = kDense ? MTd * NT : tile_base[E] * NT;
   const int per_xcd = ceil_div(total, kXcds);
@@ -132,7 +190,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   if (wid >= total) return;
 
   int e = 0, nt, row0, rows;
-  if (kDense) {
+  if constexpr (kDense) {
     nt = wid / MTd;
     row0 = (wid % MTd) * kBM;
     rows = min(kBM, T - row0);
@@ -150,16 +208,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     row0 = expert_off[e] + (rel % me) * kBM;
     rows = min(kBM, expert_off[e + 1] - row0);
   }
-  const int n0 = nt * BN;
+  const int n0 = nt * kBN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int q = lane >> 4, r16 = lane & 15;
 
   if (!kDense) {
-    for (int r = tid; r < kBM; r += kThreads) {
+    for (int r = tid; r < kBM; r += TL::kThreads) {
       const int pair = perm[row0 + min(r, rows - 1)];
       tile_pair[r] = pair;
       tile_w[r] = topk_w[pair];
@@ -170,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   // lane l lands in slot l, i.e. row 8j + l/8, physical chunk l%8, which holds
   // logical chunk (l%8) ^ (row & 7).  Rows past the tile's valid rows (or past
   // N) load a clamped row and are never stored.
-  TileCtx<kBM> c;
+  TileCtx<MOVA_TILE_ARGS> c;
 #pragma unroll
   for (int i = 0; i < TL::kLoadsA; ++i) {
     const int row = (wave * TL::kLoadsA + i) * 8 + (lane >> 3);
@@ -180,41 +238,68 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
     c.a_src[i] = reinterpret_cast<const char*>(x + (size_t)token * d) + chunk * 16;
   }
 #pragma unroll
-  for (int i = 0; i < kLoadsB; ++i) {
-    const int row = (wave * kLoadsB + i) * 8 + (lane >> 3);
+  for (int i = 0; i < TL::kLoadsB; ++i) {
+    const int row = (wave * TL::kLoadsB + i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (row & 7);
     const int n = min(n0 + row, N - 1);
     c.b_src[i] = reinterpret_cast<const char*>(W + ((size_t)e * N + n) * d) + chunk * 16;
   }
 
-  f32x4 acc[TL::kMI][4];
+  f32x4 acc[TL::kMI][TL::kNJ];
 #pragma unroll
   for (int i = 0; i < TL::kMI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TL::kNJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = d / BK;
-  issue_loads<kBM>(c, smem, wave, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const bool active = wm * (kBM / 2) < rows;  // wave-uniform
-  if (active) {
-    for (int kt = 0; kt < KT; ++kt) {
-      char* cur = smem + (kt & 1) * TL::kStage;
-      if (kt + 1 < KT)
-        issue_loads<kBM>(c, smem + ((kt + 1) & 1) * TL::kStage, wave, (kt + 1) * kRowBytes);
-      mma_step<kBM>(acc, cur, wm, wn, q, r16);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+  const bool active = wm * TL::kRowsW < rows;  // wave-uniform
+  if constexpr (kS == 2) {
+    issue_loads<MOVA_TILE_ARGS>(c, smem, wave, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (active) {
+      for (int kt = 0; kt < KT; ++kt) {
+        char* cur = smem + (kt & 1) * TL::kStage;
+        if (kt + 1 < KT)
+          issue_loads<MOVA_TILE_ARGS>(c, smem + ((kt + 1) & 1) * TL::kStage, wave,
+                                      (kt + 1) * kRowBytes);
+        mma_step<MOVA_TILE_ARGS>(acc, cur, wm, wn, q, r16);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    } else {
+      for (int kt = 0; kt < KT; ++kt) {
+        if (kt + 1 < KT)
+          issue_loads<MOVA_TILE_ARGS>(c, smem + ((kt + 1) & 1) * TL::kStage, wave,
+                                      (kt + 1) * kRowBytes);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      return;
     }
   } else {
+    // Ring of kS stages, loads kS - 1 steps ahead.  Step kt: wait for this
+    // wave's loads of step kt (the kS - 2 later steps may stay in flight) and
+    // for its LDS reads, barrier (every wave's loads of step kt have landed,
+    // and every wave is done reading step kt - 1's stage), refill that stage
+    // with step kt + kS - 1, then run step kt's MFMAs.  Steps past KT load
+    // step KT - 1 again (never read), so every step issues the same number of
+    // loads and the wait count stays exact.
+    constexpr int L = TL::kLoadsA + TL::kLoadsB;
+    __syncthreads();  // the tile's pair / weight table is written
+#pragma unroll
+    for (int st = 0; st < kS - 1; ++st)
+      issue_loads<MOVA_TILE_ARGS>(c, smem + st * TL::kStage, wave, min(st, KT - 1) * kRowBytes);
     for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT)
-        issue_loads<kBM>(c, smem + ((kt + 1) & 1) * TL::kStage, wave, (kt + 1) * kRowBytes);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kS - 2) * L));
+      raw_barrier();
+      const int nk = kt + kS - 1;
+      issue_loads<MOVA_TILE_ARGS>(c, smem + (nk % kS) * TL::kStage, wave,
+                                  min(nk, KT - 1) * kRowBytes);
+      if (active) mma_step<MOVA_TILE_ARGS>(acc, smem + (kt % kS) * TL::kStage, wm, wn, q, r16);
     }
-    return;
+    __builtin_amdgcn_s_waitcnt(0);
+    if (!active) return;
   }
 
   // Epilogue.  Grouped: y = w * SiLU(z) into the pair's partial row (fp16).
@@ -223,30 +308,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(
   for (int i = 0; i < TL::kMI; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int r = wm * (kBM / 2) + i * 16 + q * 4 + v;
+      const int r = wm * TL::kRowsW + i * 16 + q * 4 + v;
       if (r < rows) {
         if (kDense) {
-          bf16_t* dst = out + (size_t)(row0 + r) * N + n0 + wn * 64 + r16;
+          bf16_t* dst = out + (size_t)(row0 + r) * N + n0 + wn * WN + r16;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (n0 + wn * 64 + j * 16 + r16 < N) dst[j * 16] = (bf16_t)acc[i][j][v];
+          for (int j = 0; j < TL::kNJ; ++j)
+            if (n0 + wn * WN + j * 16 + r16 < N) dst[j * 16] = (bf16_t)acc[i][j][v];
         } else {
           const int pair = tile_pair[r];
           const float wt = tile_w[r];
-          f16_t* dst = partial + (size_t)pair * N + n0 + wn * 64 + r16;
+          f16_t* dst = partial + (size_t)pair * N + n0 + wn * WN + r16;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (n0 + wn * 64 + j * 16 + r16 < N) dst[j * 16] = (f16_t)(wt * siluf(acc[i][j][v]));
+          for (int j = 0; j < TL::kNJ; ++j)
+            if (n0 + wn * WN + j * 16 + r16 < N) dst[j * 16] = (f16_t)(wt * siluf(acc[i][j][v]));
         }
       }
     }
   }
 }
 
-template <int kBM, bool kDense>
+template <MOVA_TILE_PARAMS, bool kDense>
 hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) {
-  auto kern = gemm_kernel<kBM, kDense>;
-  constexpr int smem = 2 * Tile<kBM>::kStage;
+  auto kern = gemm_kernel<MOVA_TILE_ARGS, kDense>;
+  constexpr int smem = kS * Tile<MOVA_TILE_ARGS>::kStage;
+  constexpr int threads = Tile<MOVA_TILE_ARGS>::kThreads;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t err = hipFuncSetAttribute((const void*)kern,
@@ -255,29 +341,49 @@ hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) 
     attr_set = true;
   }
   const long long grid = ((tiles + kXcds - 1) / kXcds) * kXcds;
-  kern<<<dim3((unsigned)grid), kThreads, smem, stream>>>(a.x, a.W, a.perm, a.topk_w, a.expert_off,
+  kern<<<dim3((unsigned)grid), threads, smem, stream>>>(a.x, a.W, a.perm, a.topk_w, a.expert_off,
                                                          a.tile_base, a.partial, a.out, a.T, a.d,
                                                          a.N, a.E, a.k);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
-  const long long ub = (long long)gemm_max_mtiles(a.T, a.k, a.E) * ceil_div(a.N, BN);
-  return launch_tiles<kBMGrouped, false>(a, ub, stream);
+  const GemmTile t = a.tile;
+  const long long ub = (long long)gemm_max_mtiles(a.T, a.k, a.E, t.bm) * ceil_div(a.N, t.bn);
+  if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, false>(a, ub, stream);
+  if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, false>(a, ub, stream);
+  if (t.bm == 128 && t.bn == 128 && t.waves == 8) {
+    if (t.stages == 3) return launch_tiles<128, 128, 2, 4, 3, false>(a, ub, stream);
+    if (t.stages == 4) return launch_tiles<128, 128, 2, 4, 4, false>(a, ub, stream);
+    return launch_tiles<128, 128, 2, 4, 2, false>(a, ub, stream);
+  }
+  if (t.bm == 128 && t.bn == 128) return launch_tiles<128, 128, 2, 2, 4, false>(a, ub, stream);
+  return hipErrorInvalidValue;
 }
 
-int dense_gemm_block_m(int T, int N) {
-  // 256-row tiles once they fill the 256 CUs at least once; 128-row tiles
-  // (twice the workgroups) below that.
-  const long long tiles256 = (long long)ceil_div(T, 256) * ceil_div(N, BN);
-  return tiles256 >= 256 ? 256 : 128;
+GemmTile gemm_tile_dense(int T, int N) {
+  GemmTile t;
+  if (forced_tile(&t)) return t;
+  // 256 x 256 once those tiles fill the 256 CUs; below that 128 x 128, with
+  // a 4-stage ring when the grid is a single round of workgroups (one per
+  // CU, so the ring is what keeps loads in flight), else 2 stages (two
+  // workgroups per CU).
+  if ((long long)ceil_div(T, 256) * ceil_div(N, 256) >= 256) return {256, 256, 8, 2};
+  if ((long long)ceil_div(T, 128) * ceil_div(N, 128) <= 256) return {128, 128, 8, 4};
+  return {128, 128, 8, 2};
 }
 
 hipError_t launch_dense_gemm(const GemmArgs& a, hipStream_t stream) {
-  const int bm = dense_gemm_block_m(a.T, a.N);
-  const long long tiles = (long long)ceil_div(a.T, bm) * ceil_div(a.N, BN);
-  return bm == 256 ? launch_tiles<256, true>(a, tiles, stream)
-                   : launch_tiles<128, true>(a, tiles, stream);
+  const GemmTile t = gemm_tile_dense(a.T, a.N);
+  const long long tiles = (long long)ceil_div(a.T, t.bm) * ceil_div(a.N, t.bn);
+  if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, true>(a, tiles, stream);
+  if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, true>(a, tiles, stream);
+  if (t.waves == 8) {
+    if (t.stages == 3) return launch_tiles<128, 128, 2, 4, 3, true>(a, tiles, stream);
+    if (t.stages == 4) return launch_tiles<128, 128, 2, 4, 4, true>(a, tiles, stream);
+    return launch_tiles<128, 128, 2, 4, 2, true>(a, tiles, stream);
+  }
+  return launch_tiles<128, 128, 2, 2, 4, true>(a, tiles, stream);
 }
 
 }  // namespace mova

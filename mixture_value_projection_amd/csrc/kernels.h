@@ -41,24 +41,33 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
+// Tile shape of the tiled GEMM: 256 x 256, 128 x 256 or 128 x 128 (rows x
+// columns), on 8 waves (2 x 4) or, for 128 x 128, also 4 waves (2 x 2), with
+// `stages` LDS buffers (2; 3 or 4 for 128 x 128).
+struct GemmTile {
+  int bm, bn, waves, stages;
+};
+
 struct GemmArgs {
   const __bf16* x;         // [T, d]
   const __bf16* W;         // [E, N, d]
   const int32_t* perm;     // [T * k]
   const float* topk_w;     // [T * k]
   const int32_t* expert_off;
-  const int32_t* tile_base;
+  const int32_t* tile_base;  // M-tile bases for tile.bm (grouped mode)
   f16_t* partial;          // [T * k, N] (grouped mode)
   __bf16* out;             // [T, N] (dense mode)
   int T, d, N, E, k;
+  GemmTile tile;           // grouped mode; dense mode chooses its own
 };
-int gemm_block_m();
-// Upper bound on M-tiles for any routing of T tokens.
-int gemm_max_mtiles(int T, int k, int E);
+// Tile of the grouped GEMM for a call (the dispatch builds M-tiles of tile.bm rows).
+GemmTile gemm_tile_grouped(int T, int k, int E);
+// Upper bound on M-tiles of height bm for any routing of T tokens.
+int gemm_max_mtiles(int T, int k, int E, int bm);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 // Dense mode of the tiled GEMM: out = x W^T over T rows and one [N, d] weight
 // (x, W, out, T, d, N are read; the routing fields are ignored).
-int dense_gemm_block_m(int T, int N);
+GemmTile gemm_tile_dense(int T, int N);
 hipError_t launch_dense_gemm(const GemmArgs& a, hipStream_t stream);
 
 struct DenseArgs {

@@ -248,15 +248,15 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
     DecodeArgs da{xb, wb, idx, w, partial, T, d, N, E, k};
     err = launch_decode(da, stream);
   } else {
+    const GemmTile tile = gemm_tile_grouped(T, k, E);
     {
       StageScope sc(1, stream);
-      DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k,
-                      router_tile_tokens(T), gemm_block_m()};
+      DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, router_tile_tokens(T), tile.bm};
       err = launch_dispatch(dp, stream);
     }
     if (err != hipSuccess) return MOVA_ERR_HIP;
     StageScope sc(2, stream);
-    GemmArgs ga{xb, wb, perm, w, eoff, tbase, partial, nullptr, T, d, N, E, k};
+    GemmArgs ga{xb, wb, perm, w, eoff, tbase, partial, nullptr, T, d, N, E, k, tile};
     err = launch_grouped_gemm(ga, stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
@@ -324,7 +324,7 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
   } else {
     StageScope sc(4, stream);
     GemmArgs ga{(const __bf16*)x, (const __bf16*)w_v, nullptr, nullptr, nullptr, nullptr,
-                nullptr, (__bf16*)out, T, d, N, 1, 1};
+                nullptr, (__bf16*)out, T, d, N, 1, 1, {0, 0, 0, 0}};
     err = launch_dense_gemm(ga, stream);
   }
   return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;

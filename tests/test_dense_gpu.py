@@ -32,6 +32,7 @@ def _gpu_only():
     binding.load_library()
     yield
     os.environ.pop("MOVA_DENSE_PATH", None)
+    os.environ.pop("MOVA_GEMM_TILE", None)
 
 
 def dense_inputs(T, d, N, seed):
@@ -99,6 +100,23 @@ def test_dense_tiled_shapes(T, d, N):
     ref = ref_rows(x, w, rows)
     g = out if rows is None else out[torch.as_tensor(rows, device=out.device)]
     say(f"  {P.check_dense_output(g, ref, what=f'dense tiled T={T}')}")
+
+
+@pytest.mark.parametrize("T,d,N", [(300, 192, 320), (1000, 2560, 1024), (4096, 2560, 1024)])
+def test_dense_every_tile_shape(T, d, N):
+    """Each tile shape of the tiled GEMM's dense mode against the oracle, and
+    the same bits from all of them (one in-order MFMA chain per output)."""
+    x, w = dense_inputs(T, d, N, seed=T + N)
+    ref = ref_rows(x, w)
+    outs = {}
+    for tile in ("256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4"):
+        os.environ["MOVA_GEMM_TILE"] = tile
+        say(f"dense tile {tile}: T={T} d={d} N={N}")
+        outs[tile] = run_dense(x, w, "tiled")
+        os.environ.pop("MOVA_GEMM_TILE", None)
+        say(f"  {P.check_dense_output(outs[tile], ref, what=f'dense tile {tile}')}")
+    for tile, o in outs.items():
+        assert torch.equal(o, outs["256x256"]), f"{tile} differs from 256x256"
 
 
 def P_sample(T, n, seed):

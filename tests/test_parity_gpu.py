@@ -34,6 +34,7 @@ def _gpu_only():
     binding.load_library()
     yield
     os.environ.pop("MOVA_PATH", None)
+    os.environ.pop("MOVA_GEMM_TILE", None)
 
 
 def run_forward(g, k, scale, H, D, path=None):
@@ -101,6 +102,32 @@ def test_ragged_shapes_both_paths(T, d, E, k, H, D):
         a, b = outs["grouped"], outs["decode"]
         assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
         assert torch.equal(a[0], b[0])
+
+
+GEMM_TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4"]
+
+
+@pytest.mark.parametrize("T,d,E,k,H,D", [(200, 512, 16, 4, 2, 64), (700, 320, 33, 3, 3, 64),
+                                         (4096, 2560, 64, 4, 8, 128)])
+def test_grouped_gemm_every_tile_shape(T, d, E, k, H, D):
+    """Each tile shape of the grouped GEMM against the oracle; all of them (and
+    the decode path where it applies) give the same bits, since every output's
+    MFMA chain runs over the k steps in the same order."""
+    g, sh = layer(T, d, E, k, H, D, seed=T + 3 * E)
+    outs = {}
+    for tile in GEMM_TILES:
+        os.environ["MOVA_GEMM_TILE"] = tile
+        say(f"grouped tile {tile}: T={T} d={d} E={E} k={k} H={H} D={D}")
+        out, idx, w = run_forward(g, k, 2.5, H, D, "grouped")
+        os.environ.pop("MOVA_GEMM_TILE", None)
+        st = P.full_check(g, k, 2.5, H, D, out, idx, w, what=f"tile {tile}")
+        say(f"  {st}")
+        outs[tile] = out
+    if T <= 256:
+        outs["decode"] = run_forward(g, k, 2.5, H, D, "decode")[0]
+    ref = outs["256x256"]
+    for name, o in outs.items():
+        assert torch.equal(o, ref), f"{name} differs from 256x256"
 
 
 def test_widest_output_both_paths():
