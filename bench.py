@@ -161,6 +161,29 @@ def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
     return 1e6 * gsecs / gcalls, 1e6 * usecs / ucalls
 
 
+def run_rebuild(name, steps, warmup, copies):
+    """Values of the workload's tokens rebuilt from their stored routing
+    (mova_value_from_routing), as a compact cache that keeps x_t and the
+    routing instead of v_t would have to at attention time."""
+    w = inputs.WORKLOADS[name]
+    sh = w.shape
+    x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
+    cps = make_copies(sh, w.seed, w.dtype, w.bias, copies)
+    idx = torch.empty(sh.T, sh.k, dtype=torch.int32, device=DEV)
+    wt = torch.empty(sh.T, sh.k, dtype=torch.float32, device=DEV)
+    binding.value_forward(x, cps[0]["router_w"], cps[0]["router_b"], cps[0]["expert_w"], sh.k,
+                          sh.scale, sh.n_kv_heads, sh.head_dim, topk_idx=idx, topk_w=wt)
+    wt = wt.half().float()  # the compact record keeps fp16 weights
+    out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(binding.workspace_bytes(sh.T, sh.d, sh.E, sh.k, sh.n_kv_heads, sh.head_dim),
+                     dtype=torch.uint8, device=DEV)
+    calls = [(lambda c=c: binding.value_from_routing(x, idx, wt, c["expert_w"], sh.n_kv_heads,
+                                                     sh.head_dim, out=out, workspace=ws))
+             for c in cps]
+    gsecs, gcalls = graph_time(calls, steps, warmup)
+    return 1e6 * gsecs / gcalls
+
+
 def run_chunked(steps, warmup):
     """One step = the whole 65536-token stream through 4 layers (32 calls)."""
     w = inputs.WORKLOADS["chunked"]
@@ -408,6 +431,15 @@ def main():
             gqa.append(dense_line(name, rr, mova_us[name]))
             torch.cuda.empty_cache()
         line["gqa_baseline"] = gqa
+        log("compact-cache rebuild ...")
+        shp = inputs.WORKLOADS["prefill"].shape
+        rus = run_rebuild("prefill", max(5, args.steps // 10), max(2, args.warmup // 4), args.copies)
+        line["compact_cache_rebuild"] = {
+            "tokens": shp.T, "us": rus, "us_per_cached_token": rus / shp.T,
+            "bytes_per_token_value_cache": shp.N * 2,
+            "bytes_per_token_compact": shp.d * 2 + 4 + 2 * shp.k,
+            "note": "values of 4096 cached tokens rebuilt from stored x_t, top-4 ids and fp16 "
+                    "weights (no router); a value cache reads the 2 KiB rows instead"}
         log("paged decode ...")
         pus, uus = run_paged_decode(args.steps, args.warmup, args.copies)
         line["paged_decode"] = {"us_per_step": pus, "plain_us_per_step": 1e6 * step_s,

@@ -147,6 +147,34 @@ int mova_value_forward_paged(const void* x, const void* router_w, const float* r
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Value vectors rebuilt from stored routing: the expert projection, SiLU,
+ * weighting and k-way combine of mova_value_forward, with the routing given
+ * instead of computed (no router).  This is the reconstruction step of the
+ * compact cache of page "IFM K2 Horizon Deep Dive: Inside Mixture-of-Value
+ * Attention (MoVA) ...", section "The Two Architectural Caching Strategies
+ * for MoVA", Option B, which keeps a token's input x_t with its top-4 expert
+ * ids and 4 weights and materialises the value vector when it is needed:
+ *
+ *   out[t, h, j] = sum over i < k with 0 <= topk_idx[t,i] < E of
+ *                  topk_w[t,i] * SiLU( sum_c x[t,c] * expert_w[topk_idx[t,i], h*head_dim + j, c] )
+ *
+ *   x        bf16  [T, d]    the stored inputs
+ *   topk_idx int32 [T, k]    stored expert ids; an id outside [0, E) marks an
+ *                            unused slot, which adds nothing (so does a 0 weight)
+ *   topk_w   float [T, k]    stored weights (widen fp16 weights to float)
+ *   expert_w, out, workspace (mova_workspace_bytes) as for mova_value_forward.
+ *
+ * Ids may repeat within a token (each slot counts).  Numerics as for
+ * mova_value_forward; fed the routing that mova_value_forward reported, it
+ * returns the same bits.  Errors as for mova_value_forward (topk_idx and
+ * topk_w are required, 16-byte aligned).
+ */
+int mova_value_from_routing(const void* x, const int32_t* topk_idx, const float* topk_w,
+                            const void* expert_w, int T, int d, int E, int k, int n_kv_heads,
+                            int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * Bytes of device workspace mova_dense_value_proj needs for these sizes: 0
  * when T == 0 or T > 256, (size_t)-1 outside the supported domain (that of
  * mova_value_forward without the router's E and k).

@@ -50,6 +50,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mova_value_forward_paged.restype = i
     lib.mova_value_forward_paged.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, i, i, vp, vp,
                                              vp, vp, vp, sz, vp]
+    lib.mova_value_from_routing.restype = i
+    lib.mova_value_from_routing.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, sz, vp]
     lib.mova_dense_workspace_bytes.restype = sz
     lib.mova_dense_workspace_bytes.argtypes = [i, i, i, i]
     lib.mova_dense_value_proj.restype = i
@@ -209,6 +211,42 @@ def value_forward_paged(x: torch.Tensor, router_w: torch.Tensor, router_b: Optio
                                       _ptr(workspace), workspace.numel(), _stream(dev))
     if rc != MOVA_OK:
         raise MovaError(rc, "mova_value_forward_paged")
+    return out
+
+
+def value_from_routing(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                       expert_w: torch.Tensor, n_kv_heads: Optional[int] = None,
+                       head_dim: int = 128, out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mova_value_from_routing: value vectors rebuilt from stored inputs and
+    stored routing (int32 ids, float32 weights [T, k]); ids outside [0, E)
+    mark unused slots.  Returns bf16 [T, n_kv_heads, head_dim]."""
+    lib = load_library()
+    T, d = x.shape
+    E, N, d2 = expert_w.shape
+    k = topk_idx.shape[1] if topk_idx.dim() == 2 else -1
+    if d2 != d:
+        raise ValueError("expert_w's last dim must equal x's width")
+    if n_kv_heads is None:
+        n_kv_heads = N // head_dim
+    if n_kv_heads * head_dim != N:
+        raise ValueError("n_kv_heads * head_dim must equal the expert width")
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    _check(expert_w, "expert_w", torch.bfloat16, (E, N, d), dev)
+    if out is None:
+        out = torch.empty(T, n_kv_heads, head_dim, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, n_kv_heads, head_dim), dev)
+    nbytes = workspace_bytes(T, d, E, k, n_kv_heads, head_dim)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = lib.mova_value_from_routing(_ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(expert_w), T, d,
+                                     E, k, n_kv_heads, head_dim, _ptr(out), _ptr(workspace),
+                                     workspace.numel(), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_value_from_routing")
     return out
 
 

@@ -20,12 +20,15 @@ namespace mova {
 
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
-template <bool kPaged>
+// kMasked: the routing came from the caller, and a slot whose expert id is
+// outside [0, E) has no partial row; it is skipped (adds nothing).
+template <bool kPaged, bool kMasked>
 __global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ partial,
                                                       bf16_t* __restrict__ out, int T, int N, int k,
                                                       const int64_t* __restrict__ slot,
                                                       long long num_slots,
-                                                      bf16_t* __restrict__ cache) {
+                                                      bf16_t* __restrict__ cache,
+                                                      const int32_t* __restrict__ idx, int E) {
   const int vec_per_row = N / 8;
   const long long total = (long long)T * vec_per_row;
   for (long long v = blockIdx.x * 256ll + threadIdx.x; v < total; v += (long long)gridDim.x * 256) {
@@ -33,15 +36,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ 
     const int c = (int)(v % vec_per_row) * 8;
     const f16_t* src = partial + (size_t)t * k * N + c;
     float s[8];
-    {
+    if (!kMasked) {
       const f16x8 h = __builtin_bit_cast(f16x8, load16(src));
 #pragma unroll
       for (int i = 0; i < 8; ++i) s[i] = (float)h[i];
-    }
-    for (int j = 1; j < k; ++j) {
-      const f16x8 h = __builtin_bit_cast(f16x8, load16(src + (size_t)j * N));
+      for (int j = 1; j < k; ++j) {
+        const f16x8 h2 = __builtin_bit_cast(f16x8, load16(src + (size_t)j * N));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s[i] += (float)h[i];
+        for (int i = 0; i < 8; ++i) s[i] += (float)h2[i];
+      }
+    } else {
+      // Same sum over the valid slots, in slot order; the first valid slot is
+      // assigned rather than added to 0, so with every id valid the bits
+      // equal the unmasked sum (a -0 partial stays -0).
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s[i] = 0.f;
+      bool first = true;
+      for (int j = 0; j < k; ++j) {
+        const int e = idx[(size_t)t * k + j];
+        if (e < 0 || e >= E) continue;
+        const f16x8 h2 = __builtin_bit_cast(f16x8, load16(src + (size_t)j * N));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] = first ? (float)h2[i] : s[i] + (float)h2[i];
+        first = false;
+      }
     }
     u32x4 packed;
 #pragma unroll
@@ -60,12 +78,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const long long total = (long long)a.T * (a.N / 8);
   const long long blocks = std::min<long long>((total + 255) / 256, 256ll * 16);
-  if (a.cache == nullptr)
-    combine_kernel<false><<<dim3((unsigned)blocks), 256, 0, stream>>>(a.partial, a.out, a.T, a.N,
-                                                                      a.k, nullptr, 0, nullptr);
+  const dim3 grid((unsigned)blocks);
+  if (a.idx != nullptr)
+    combine_kernel<false, true><<<grid, 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k,
+                                                          nullptr, 0, nullptr, a.idx, a.E);
+  else if (a.cache == nullptr)
+    combine_kernel<false, false><<<grid, 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k,
+                                                           nullptr, 0, nullptr, nullptr, 0);
   else
-    combine_kernel<true><<<dim3((unsigned)blocks), 256, 0, stream>>>(
-        a.partial, a.out, a.T, a.N, a.k, a.slot, a.num_slots, a.cache);
+    combine_kernel<true, false><<<grid, 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k, a.slot,
+                                                          a.num_slots, a.cache, nullptr, 0);
   return hipGetLastError();
 }
 

@@ -51,8 +51,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
     f16_t* __restrict__ partial, int T, int d, int N, int E, int k) {
-  __shared__ int plist[kDecodeMaxT];
-  __shared__ float wlist[kDecodeMaxT];
+  // An expert gets at most T * k pairs (k of them per token when a caller's
+  // stored routing repeats an id; the router never does).
+  __shared__ int plist[kDecodeMaxT * kMaxTopK];
+  __shared__ float wlist[kDecodeMaxT * kMaxTopK];
   __shared__ int wave_hits[4];
 
   const int slices = ceil_div(N, kSlice);
@@ -86,8 +88,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   load_w(b0, 0);
   if (nb > 1) load_w(b1, 1);
 
-  // Pairs routed to this expert, in pair order (a token picks e at most once),
-  // with their routing weights, 256 pairs per round: each thread reads one
+  // Pairs routed to this expert, in pair order, with their routing weights,
+  // 256 pairs per round: each thread reads one
   // pair's expert id and weight, and the hits are ranked by wave ballots.
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int ce = 0;

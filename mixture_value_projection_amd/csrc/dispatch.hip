@@ -6,6 +6,8 @@
 // count (chunk = one router workgroup's tokens).  Two kernels finish the job
 // without atomics on global memory:
 //
+//   count:   (only when the routing comes from the caller instead of the
+//            router) the per-chunk, per-expert counts;
 //   scan:    per expert, exclusive prefix of the counts over chunks (in
 //            place), expert offsets, and the first M-tile of each expert;
 //   scatter: each chunk re-reads its routing and writes every pair id
@@ -14,7 +16,8 @@
 //
 // The result is stable: within an expert, pairs appear in increasing pair id,
 // so the GEMM's row order -- and hence every output bit -- is independent of
-// scheduling.
+// scheduling.  A pair whose expert id lies outside [0, E) is not counted and
+// not placed (caller-supplied routing); the router never produces one.
 #include "common.h"
 #include "kernels.h"
 
@@ -112,8 +115,9 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = 0; base < npairs; base += 256) {
     const int p = base + threadIdx.x;
-    const bool valid = p < npairs;
-    const int e = valid ? idx[p0 + p] : 0;
+    const int e_raw = p < npairs ? idx[p0 + p] : 0;
+    const bool valid = p < npairs && e_raw >= 0 && e_raw < E;
+    const int e = valid ? e_raw : 0;
     // Lanes of this wave holding the same expert (6 ballots over the id bits).
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -138,6 +142,32 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     }
     __syncthreads();
   }
+}
+
+// Per-chunk expert counts of caller-supplied routing: one workgroup per chunk,
+// LDS histogram (integer counts, so the order of the atomics does not matter).
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ counts, int T,
+                                                             int E, int k, int chunk_tokens) {
+  __shared__ int hist[kMaxExperts];
+  const int c = blockIdx.x;
+  const int p0 = c * chunk_tokens * k;
+  const int npairs = min(T * k, p0 + chunk_tokens * k) - p0;
+  if (threadIdx.x < kMaxExperts) hist[threadIdx.x] = 0;
+  __syncthreads();
+  for (int p = threadIdx.x; p < npairs; p += 256) {
+    const int e = idx[p0 + p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  if (threadIdx.x < E) counts[(size_t)c * E + threadIdx.x] = hist[threadIdx.x];
+}
+
+hipError_t launch_dispatch_count(const DispatchArgs& a, hipStream_t stream) {
+  const int C = ceil_div(a.T, a.chunk_tokens);
+  dispatch_count_kernel<<<C, 256, 0, stream>>>(a.idx, a.chunk_counts, a.T, a.E, a.k,
+                                               a.chunk_tokens);
+  return hipGetLastError();
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {

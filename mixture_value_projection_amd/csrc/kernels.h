@@ -40,6 +40,9 @@ struct DispatchArgs {
   int block_m;       // M-tile height of the grouped GEMM
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
+// chunk_counts from idx (routing supplied by the caller rather than the router);
+// ids outside [0, E) are not counted.
+hipError_t launch_dispatch_count(const DispatchArgs& a, hipStream_t stream);
 
 // Tile shape of the tiled GEMM: 256 x 256, 128 x 256 or 128 x 128 (rows x
 // columns), on 8 waves (2 x 4) or, for 128 x 128, also 4 waves (2 x 2), with
@@ -104,6 +107,11 @@ struct CombineArgs {
   const int64_t* slot = nullptr;
   long long num_slots = 0;
   __bf16* cache = nullptr;
+  // Caller-supplied routing (null = router output): slot i of token t is
+  // skipped when idx[t * k + i] is outside [0, E) (its partial row is never
+  // written).
+  const int32_t* idx = nullptr;
+  int E = 0;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

@@ -190,14 +190,21 @@ int mova_route(const void* x, const void* router_w, const float* router_b, int T
   return launch_router_tile(ra, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }
 
-// Shared body of mova_value_forward and mova_value_forward_paged.  `pg` set:
-// the combine also stores each row at its slot of the paged pool, and `out`
-// may be null.
+// Shared body of mova_value_forward, mova_value_forward_paged and
+// mova_value_from_routing.  `pg` set: the combine also stores each row at its
+// slot of the paged pool, and `out` may be null.  `given` set: the routing
+// is the caller's (no router; ids outside [0, E) are skipped), router_w,
+// router_b and scale are unused.
+struct GivenRouting {
+  const int32_t* idx;
+  const float* w;
+};
 static int value_forward_impl(const void* x, const void* router_w, const float* router_b,
                               const void* expert_w, int T, int d, int E, int k, float scale,
                               int n_kv_heads, int head_dim, void* out, const PagedStore* pg,
                               int32_t* topk_idx_out, float* topk_w_out, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
+                              size_t workspace_bytes, hipStream_t stream,
+                              const GivenRouting* given = nullptr) {
   int rc = check_shape(T, d, E, k);
   if (rc != MOVA_OK) return rc;
   rc = check_heads(n_kv_heads, head_dim);
@@ -207,7 +214,11 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
   if (pg != nullptr && (long long)pg->num_blocks * pg->block_size > kMaxSlots)
     return MOVA_ERR_UNSUPPORTED;
   if (T == 0) return MOVA_OK;
-  if (x == nullptr || router_w == nullptr || expert_w == nullptr || (out == nullptr && pg == nullptr))
+  if (given != nullptr && (given->idx == nullptr || given->w == nullptr)) return MOVA_ERR_INVALID_ARG;
+  if (given != nullptr && (!aligned16(given->idx) || !aligned16(given->w)))
+    return MOVA_ERR_INVALID_ARG;
+  if (x == nullptr || (router_w == nullptr && given == nullptr) || expert_w == nullptr ||
+      (out == nullptr && pg == nullptr))
     return MOVA_ERR_INVALID_ARG;
   if (pg != nullptr && (pg->cache == nullptr || pg->slot == nullptr)) return MOVA_ERR_INVALID_ARG;
   if (pg != nullptr && (!aligned16(pg->cache) || ((uintptr_t)pg->slot & 7u) != 0))
@@ -221,8 +232,9 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
   if (((uintptr_t)workspace & 255u) != 0) return MOVA_ERR_INVALID_ARG;
 
   char* ws = (char*)workspace;
-  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(ws + L.idx);
-  float* w = topk_w_out ? topk_w_out : (float*)(ws + L.w);
+  int32_t* idx = given ? const_cast<int32_t*>(given->idx)
+                       : (topk_idx_out ? topk_idx_out : (int32_t*)(ws + L.idx));
+  float* w = given ? const_cast<float*>(given->w) : (topk_w_out ? topk_w_out : (float*)(ws + L.w));
   int32_t* chunk = (int32_t*)(ws + L.chunk);
   int32_t* eoff = (int32_t*)(ws + L.eoff);
   int32_t* tbase = (int32_t*)(ws + L.tbase);
@@ -234,8 +246,8 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
 
   const Path path = choose_path(T, k);
   const bool grouped = path == Path::Grouped;
-  hipError_t err;
-  {
+  hipError_t err = hipSuccess;
+  if (given == nullptr) {
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w,
                   grouped ? chunk : nullptr};
@@ -252,7 +264,8 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
     {
       StageScope sc(1, stream);
       DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, router_tile_tokens(T), tile.bm};
-      err = launch_dispatch(dp, stream);
+      if (given != nullptr) err = launch_dispatch_count(dp, stream);
+      if (err == hipSuccess) err = launch_dispatch(dp, stream);
     }
     if (err != hipSuccess) return MOVA_ERR_HIP;
     StageScope sc(2, stream);
@@ -263,6 +276,10 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
   {
     StageScope sc(3, stream);
     CombineArgs ca{partial, (__bf16*)out, T, N, k};
+    if (given != nullptr) {
+      ca.idx = given->idx;
+      ca.E = E;
+    }
     if (pg != nullptr) {
       ca.slot = pg->slot;
       ca.num_slots = (long long)pg->num_blocks * pg->block_size;
@@ -281,6 +298,16 @@ int mova_value_forward(const void* x, const void* router_w, const float* router_
   return value_forward_impl(x, router_w, router_b, expert_w, T, d, E, k, scale, n_kv_heads,
                             head_dim, out, nullptr, topk_idx_out, topk_w_out, workspace,
                             workspace_bytes, stream);
+}
+
+int mova_value_from_routing(const void* x, const int32_t* topk_idx, const float* topk_w,
+                            const void* expert_w, int T, int d, int E, int k, int n_kv_heads,
+                            int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  const GivenRouting given{topk_idx, topk_w};
+  return value_forward_impl(x, nullptr, nullptr, expert_w, T, d, E, k, 1.0f, n_kv_heads, head_dim,
+                            out, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+                            &given);
 }
 
 int mova_value_forward_paged(const void* x, const void* router_w, const float* router_b,

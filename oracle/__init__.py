@@ -12,7 +12,8 @@ Parity status per function (details in the module docstring of
 * ``router_logits``, ``sigmoid``, ``route`` (except the bias role and the
   router's reduction order), ``combine_experts``, ``value_forward`` and
   ``dense_value_proj`` (the matched dense baseline) and
-  ``paged_value_write`` (the paged cache store): pinned by the tests in
+  ``paged_value_write`` (the paged cache store) and ``rebuild_values`` (the
+  compact cache's reconstruction): pinned by the tests in
   ``tests/test_oracle_pins.py``;
 * the role of the router bias (added to the scores for selection only) and
   the router's summation order: parity unpinned -- no page prints a value
@@ -24,6 +25,7 @@ from .mova_oracle import (  # noqa: F401
     combine_experts,
     dense_value_proj,
     paged_value_write,
+    rebuild_values,
     route,
     router_logits,
     sigmoid,

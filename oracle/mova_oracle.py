@@ -198,3 +198,32 @@ def paged_value_write(cache, values, slot_mapping) -> np.ndarray:
         if 0 <= s < nb * bs:
             out[s // bs, s % bs] = vals[t]
     return out
+
+
+def rebuild_values(x, expert_w, idx, w) -> np.ndarray:
+    """Value vectors rebuilt from a token's stored input and stored routing
+    (Option B of the page "IFM K2 Horizon Deep Dive: Inside Mixture-of-Value
+    Attention (MoVA) ...", section "The Two Architectural Caching Strategies
+    for MoVA": the cache keeps x_t with the top-4 expert ids and 4 weights and
+    materialises v_t when attention needs it).
+
+    The same per-slot loop as ``combine_experts`` (page 2, "Where the routing
+    happens": SiLU of each chosen expert's projection, weighted, summed),
+    except that the routing is given.  Reading (the page does not say how an
+    unused slot is marked): a slot whose id lies outside [0, E) adds nothing;
+    ids may repeat, each slot counting once.  Returns [T, N] float64.
+    """
+    x = _f64(x)
+    W = _f64(expert_w)
+    idx = np.asarray(idx)
+    w = _f64(w)
+    E = W.shape[0]
+    out = np.zeros((x.shape[0], W.shape[1]))
+    for t in range(x.shape[0]):
+        for j in range(idx.shape[1]):
+            e = int(idx[t, j])
+            if not 0 <= e < E:
+                continue
+            z = W[e] @ x[t]
+            out[t] += w[t, j] * silu(z)
+    return out

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
     for n in ("mova_route", "mova_value_forward", "mova_workspace_bytes", "mova_status_str",
               "mova_version", "mova_timing_enable", "mova_timing_read",
               "mova_dense_value_proj", "mova_dense_workspace_bytes",
-              "mova_value_forward_paged"):
+              "mova_value_forward_paged", "mova_value_from_routing"):
         assert n in names
 
 
@@ -145,6 +145,30 @@ def test_paged_rejects(lib, kw, rc):
 
 def test_paged_empty_is_noop(lib):
     assert paged(lib, T=0, x=None, cache=None, slot=None, ws=None, wsb=0) == OK
+
+
+def rebuild(lib, **kw):
+    a = dict(x=FAKE, idx=FAKE, w=FAKE, ew=FAKE, T=16, d=256, E=8, k=2, H=2, D=32, out=FAKE,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mova_value_from_routing(a["x"], a["idx"], a["w"], a["ew"], a["T"], a["d"], a["E"],
+                                       a["k"], a["H"], a["D"], a["out"], a["ws"], a["wsb"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), INVALID), (dict(E=65), UNSUPPORTED), (dict(k=9, E=16), UNSUPPORTED),
+    (dict(d=100), UNSUPPORTED), (dict(idx=None), INVALID), (dict(w=None), INVALID),
+    (dict(idx=FAKE + 4), INVALID), (dict(w=FAKE + 8), INVALID), (dict(x=None), INVALID),
+    (dict(ew=None), INVALID), (dict(out=None), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(wsb=1024), WORKSPACE),
+])
+def test_rebuild_rejects(lib, kw, rc):
+    assert rebuild(lib, **kw) == rc
+
+
+def test_rebuild_empty_is_noop(lib):
+    assert rebuild(lib, T=0, x=None, idx=None, w=None, out=None, ws=None, wsb=0) == OK
 
 
 def test_dense_workspace_bytes(lib):

@@ -327,6 +327,39 @@ def test_paged_write_permutation_round_trip():
     assert (flat[rest] == -7.0).all()
 
 
+# -------------------------------------- values rebuilt from stored routing
+
+def test_rebuild_hand_example():
+    """Worked by hand: expert 1 swaps the two inputs, slot 2's id (5) is past
+    E = 2 and adds nothing.  z = (-2, 1), out = 2 * (silu(-2), silu(1)) with
+    silu(z) = z / (1 + exp(-z))."""
+    W = np.array([[[1.0, 0.0], [0.0, 1.0]], [[0.0, 1.0], [1.0, 0.0]]])
+    x = np.array([[1.0, -2.0]])
+    got = oracle.rebuild_values(x, W, [[1, 5]], [[2.0, 9.0]])
+    want = [[2.0 * (-2.0) / (1.0 + math.exp(2.0)), 2.0 * 1.0 / (1.0 + math.exp(-1.0))]]
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=0)
+
+
+def test_rebuild_from_own_routing_matches_brute_force():
+    """Rebuilding with the routing the method chose reproduces the independent
+    dense-masked evaluation of the whole layer."""
+    x, wr, b, W = rand_layer(6, 24, 8, 3, 10, seed=31)
+    ref, _ = brute_force(x, wr, b, W, 3, 2.5)
+    r = oracle.route(x, wr, b, 3, 2.5)
+    np.testing.assert_allclose(oracle.rebuild_values(x, W, r.idx, r.w), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_rebuild_repeated_and_negative_ids():
+    """A repeated id counts once per slot; -1 marks an unused slot."""
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((3, 16))
+    W = rng.standard_normal((4, 8, 16)) / 4
+    one = oracle.rebuild_values(x, W, [[2, -1]] * 3, [[1.0, 5.0]] * 3)
+    two = oracle.rebuild_values(x, W, [[2, 2]] * 3, [[0.25, 0.75]] * 3)
+    np.testing.assert_allclose(two, one, rtol=1e-13, atol=1e-15)
+    assert (oracle.rebuild_values(x, W, [[-1, 4]] * 3, [[1.0, 1.0]] * 3) == 0).all()
+
+
 def test_skewed_workload_load_ratio():
     """The skewed workload's bias gives max / mean expert load of 10 (+-5%)."""
     w = inputs.WORKLOADS["skewed"]
