@@ -184,6 +184,46 @@ def run_rebuild(name, steps, warmup, copies):
     return 1e6 * gsecs / gcalls
 
 
+def run_ffn(name, steps, warmup, copies=2):
+    """The FFN mixture of experts (100 SwiGLU experts of width 768, top-8, one
+    shared expert) at a workload's token count; expert weights rotated over
+    `copies` device copies (1.2 GB each)."""
+    sh = inputs.FFN_WORKLOADS[name]
+    L = inputs.make_ffn_layer(sh, 0)
+    x = L["x"].to(DEV)
+    layers = []
+    for c in range(copies):
+        g = {k: v.to(DEV) for k, v in L.items() if k != "x"}
+        g["gate_up_w"] = binding.ffn_pack_gate_up(g.pop("gate_w"), g.pop("up_w"))
+        g["shared_gate_up_w"] = binding.ffn_pack_gate_up(g.pop("shared_gate_w"),
+                                                         g.pop("shared_up_w"))
+        layers.append(g)
+    out = torch.empty(sh.T, sh.d, dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty(sh.T, sh.k, dtype=torch.int32, device=DEV)
+    ws = torch.empty(binding.ffn_workspace_bytes(sh.T, sh.d, sh.E, sh.k, sh.inter, sh.inter_shared),
+                     dtype=torch.uint8, device=DEV)
+    binding.ffn_moe_forward(x, layers[0]["router_w"], layers[0]["router_b"],
+                            layers[0]["gate_up_w"], layers[0]["down_w"], sh.k, sh.scale,
+                            layers[0]["shared_gate_up_w"], layers[0]["shared_down_w"], out=out,
+                            topk_idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    touched = int((np.bincount(idx.cpu().numpy().ravel(), minlength=sh.E) > 0).sum())
+    calls = [(lambda g=g: binding.ffn_moe_forward(
+        x, g["router_w"], g["router_b"], g["gate_up_w"], g["down_w"], sh.k, sh.scale,
+        g["shared_gate_up_w"], g["shared_down_w"], out=out, workspace=ws)) for g in layers]
+    gsecs, gcalls = graph_time(calls, steps, warmup)
+    us = 1e6 * gsecs / gcalls
+    flops = 2.0 * sh.T * (3 * sh.d * (sh.k * sh.inter + sh.inter_shared) + sh.d * sh.E)
+    wbytes = 2.0 * 3 * sh.d * (touched * sh.inter + sh.inter_shared) + 2.0 * sh.E * sh.d
+    del layers, calls
+    return {"workload": name, "T": sh.T, "d": sh.d, "E": sh.E, "k": sh.k, "inter": sh.inter,
+            "inter_shared": sh.inter_shared, "touched_experts": touched, "us_per_call": us,
+            "tokens_per_s": sh.T / (us * 1e-6), "tflops": flops / (us * 1e-6) / 1e12,
+            "frac_bf16_peak": flops / (us * 1e-6) / accounting.BF16_MFMA_PEAK_FLOPS,
+            "weight_GB_per_s": wbytes / (us * 1e-6) / 1e9,
+            "frac_hbm_weights": wbytes / (us * 1e-6) / accounting.HBM_PEAK_BPS}
+
+
 def run_chunked(steps, warmup):
     """One step = the whole 65536-token stream through 4 layers (32 calls)."""
     w = inputs.WORKLOADS["chunked"]
@@ -431,6 +471,10 @@ def main():
             gqa.append(dense_line(name, rr, mova_us[name]))
             torch.cuda.empty_cache()
         line["gqa_baseline"] = gqa
+        log("FFN mixture of experts ...")
+        line["ffn_moe"] = [run_ffn("ffn_decode", args.steps, args.warmup),
+                           run_ffn("ffn_prefill", max(5, args.steps // 10), max(2, args.warmup // 4))]
+        torch.cuda.empty_cache()
         log("compact-cache rebuild ...")
         shp = inputs.WORKLOADS["prefill"].shape
         rus = run_rebuild("prefill", max(5, args.steps // 10), max(2, args.warmup // 4), args.copies)

@@ -209,6 +209,57 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
                           hipStream_t stream);
 
 /*
+ * FFN mixture of experts on the same dispatch and tiled-GEMM kernels: the
+ * sparse FFN the model runs beside its routed value projection, 100 experts
+ * with top-8 routing plus one shared expert (the thevalue.engineering page
+ * on the MoVA architecture, section "Dual sparsity").  The pages give neither
+ * the FFN expert shape nor its routing function; readings taken here:
+ *   - SwiGLU experts, down( SiLU(gate x) * (up x) ), bias-free, of width
+ *     `inter` (routed) and `inter_shared` (shared; 0 = no shared expert);
+ *   - routing by the value router's function (sigmoid scores, bias added for
+ *     selection, top-k, scores renormalised and multiplied by `scale`);
+ *   - out = sum_i w_i * expert_{idx_i}(x) + shared(x), one [d] row per token.
+ *
+ *   x                bf16  [T, d]
+ *   router_w         bf16  [E, d];  router_b float [E] or NULL
+ *   gate_up_w        bf16  [E, 2*inter, d]  gate and up rows interleaved in
+ *                    blocks of 16 (see mova_ffn_pack_gate_up)
+ *   down_w           bf16  [E, d, inter]
+ *   shared_gate_up_w bf16  [2*inter_shared, d] (interleaved the same way)
+ *   shared_down_w    bf16  [d, inter_shared]
+ *   out              bf16  [T, d]
+ *   topk_idx_out / topk_w_out  int32 / float [T, k], optional
+ *   workspace        >= mova_ffn_workspace_bytes(...) bytes, 256-byte aligned
+ *
+ * Domain: 1 <= E <= 128, 1 <= k <= min(E, 8), d % 64 == 0 and d <= 16384,
+ * inter and inter_shared multiples of 64 up to 16384 (inter > 0), T <= 2^24.
+ * Numerics: products accumulate in fp32; SiLU(gate) * up is rounded once to
+ * bf16 (the down projection's MFMA operand); each routed slot's w * down(h)
+ * and the shared expert's output are kept as fp16; the sum is fp32 in slot
+ * order, the shared term last, rounded once to bf16.  Logits for the top-k
+ * are one fp32 MFMA chain per (token, expert) over d in order.  Errors as for
+ * mova_value_forward.
+ */
+size_t mova_ffn_workspace_bytes(int T, int d, int E, int k, int inter, int inter_shared);
+
+/*
+ * gate_up_w[e, 32b + j] = gate_w[e, 16b + j] and gate_up_w[e, 32b + 16 + j] =
+ * up_w[e, 16b + j] for j < 16: the row order the FFN forward reads.  gate_w
+ * and up_w are bf16 [E, inter, d] (nn.Linear layout); gate_up_w is bf16
+ * [E, 2*inter, d] and must not overlap them.  Pass E = 1 for the shared
+ * expert.  Domain as mova_ffn_moe_forward; returns MOVA_OK or an error.
+ */
+int mova_ffn_pack_gate_up(const void* gate_w, const void* up_w, int E, int inter, int d,
+                          void* gate_up_w, hipStream_t stream);
+
+int mova_ffn_moe_forward(const void* x, const void* router_w, const float* router_b,
+                         const void* gate_up_w, const void* down_w, int E, int k, int inter,
+                         const void* shared_gate_up_w, const void* shared_down_w,
+                         int inter_shared, int T, int d, float scale, void* out,
+                         int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Stage timing (profiling aid).  While enabled, each mova_value_forward call
  * records a HIP event pair on the call's stream around each stage selected
  * by `stage_mask` (bit s = stage s), for up to `capacity` calls.  Stages:

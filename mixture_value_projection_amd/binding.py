@@ -52,6 +52,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                              vp, vp, vp, sz, vp]
     lib.mova_value_from_routing.restype = i
     lib.mova_value_from_routing.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, sz, vp]
+    lib.mova_ffn_workspace_bytes.restype = sz
+    lib.mova_ffn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mova_ffn_pack_gate_up.restype = i
+    lib.mova_ffn_pack_gate_up.argtypes = [vp, vp, i, i, i, vp, vp]
+    lib.mova_ffn_moe_forward.restype = i
+    lib.mova_ffn_moe_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp, vp, i, i, i, f, vp, vp,
+                                         vp, vp, sz, vp]
     lib.mova_dense_workspace_bytes.restype = sz
     lib.mova_dense_workspace_bytes.argtypes = [i, i, i, i]
     lib.mova_dense_value_proj.restype = i
@@ -247,6 +254,77 @@ def value_from_routing(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Te
                                      workspace.numel(), _stream(dev))
     if rc != MOVA_OK:
         raise MovaError(rc, "mova_value_from_routing")
+    return out
+
+
+def ffn_workspace_bytes(T: int, d: int, E: int, k: int, inter: int, inter_shared: int) -> int:
+    n = load_library().mova_ffn_workspace_bytes(T, d, E, k, inter, inter_shared)
+    if n == ctypes.c_size_t(-1).value:
+        raise MovaError(-2, "mova_ffn_workspace_bytes")
+    return n
+
+
+def ffn_pack_gate_up(gate_w: torch.Tensor, up_w: torch.Tensor) -> torch.Tensor:
+    """mova_ffn_pack_gate_up: bf16 [E, inter, d] gate and up weights (or
+    [inter, d] for the shared expert) -> the interleaved [E, 2 inter, d]
+    (or [2 inter, d]) layout the FFN forward reads."""
+    lib = load_library()
+    squeeze = gate_w.dim() == 2
+    g = gate_w.unsqueeze(0) if squeeze else gate_w
+    u = up_w.unsqueeze(0) if squeeze else up_w
+    E, inter, d = g.shape
+    _check(g, "gate_w", torch.bfloat16, (E, inter, d), g.device)
+    _check(u, "up_w", torch.bfloat16, (E, inter, d), g.device)
+    dst = torch.empty(E, 2 * inter, d, dtype=torch.bfloat16, device=g.device)
+    rc = lib.mova_ffn_pack_gate_up(_ptr(g), _ptr(u), E, inter, d, _ptr(dst), _stream(g.device))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_ffn_pack_gate_up")
+    return dst[0] if squeeze else dst
+
+
+def ffn_moe_forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor],
+                    gate_up_w: torch.Tensor, down_w: torch.Tensor, k: int, scale: float,
+                    shared_gate_up_w: Optional[torch.Tensor] = None,
+                    shared_down_w: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                    topk_w: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mova_ffn_moe_forward: returns bf16 [T, d].  gate_up_w comes from
+    ``ffn_pack_gate_up``; the shared expert is optional."""
+    lib = load_library()
+    T, d = x.shape
+    E, two_inter, d2 = gate_up_w.shape
+    inter = two_inter // 2
+    if d2 != d:
+        raise ValueError("gate_up_w's last dim must equal x's width")
+    inter_s = 0 if shared_gate_up_w is None else shared_gate_up_w.shape[0] // 2
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(router_w, "router_w", torch.bfloat16, (E, d), dev)
+    if router_b is not None:
+        _check(router_b, "router_b", torch.float32, (E,), dev)
+    _check(gate_up_w, "gate_up_w", torch.bfloat16, (E, 2 * inter, d), dev)
+    _check(down_w, "down_w", torch.bfloat16, (E, d, inter), dev)
+    if inter_s:
+        _check(shared_gate_up_w, "shared_gate_up_w", torch.bfloat16, (2 * inter_s, d), dev)
+        _check(shared_down_w, "shared_down_w", torch.bfloat16, (d, inter_s), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, d), dev)
+    if topk_idx is not None:
+        _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    if topk_w is not None:
+        _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    nbytes = ffn_workspace_bytes(T, d, E, k, inter, inter_s)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = lib.mova_ffn_moe_forward(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(gate_up_w),
+                                  _ptr(down_w), E, k, inter, _ptr(shared_gate_up_w),
+                                  _ptr(shared_down_w), inter_s, T, d, float(scale), _ptr(out),
+                                  _ptr(topk_idx), _ptr(topk_w), _ptr(workspace), workspace.numel(),
+                                  _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_ffn_moe_forward")
     return out
 
 

@@ -22,13 +22,16 @@ typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
 // kMasked: the routing came from the caller, and a slot whose expert id is
 // outside [0, E) has no partial row; it is skipped (adds nothing).
+// extra (unmasked form only; may be null): a [T, N] fp16 term added after the
+// k slots -- the FFN's shared expert.
 template <bool kPaged, bool kMasked>
 __global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ partial,
                                                       bf16_t* __restrict__ out, int T, int N, int k,
                                                       const int64_t* __restrict__ slot,
                                                       long long num_slots,
                                                       bf16_t* __restrict__ cache,
-                                                      const int32_t* __restrict__ idx, int E) {
+                                                      const int32_t* __restrict__ idx, int E,
+                                                      const f16_t* __restrict__ extra) {
   const int vec_per_row = N / 8;
   const long long total = (long long)T * vec_per_row;
   for (long long v = blockIdx.x * 256ll + threadIdx.x; v < total; v += (long long)gridDim.x * 256) {
@@ -42,6 +45,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const f16_t* __restrict__ 
       for (int i = 0; i < 8; ++i) s[i] = (float)h[i];
       for (int j = 1; j < k; ++j) {
         const f16x8 h2 = __builtin_bit_cast(f16x8, load16(src + (size_t)j * N));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[i] += (float)h2[i];
+      }
+      if (extra != nullptr) {
+        const f16x8 h2 = __builtin_bit_cast(f16x8, load16(extra + (size_t)t * N + c));
 #pragma unroll
         for (int i = 0; i < 8; ++i) s[i] += (float)h2[i];
       }
@@ -81,13 +89,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)blocks);
   if (a.idx != nullptr)
     combine_kernel<false, true><<<grid, 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k,
-                                                          nullptr, 0, nullptr, a.idx, a.E);
+                                                          nullptr, 0, nullptr, a.idx, a.E, nullptr);
   else if (a.cache == nullptr)
     combine_kernel<false, false><<<grid, 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k,
-                                                           nullptr, 0, nullptr, nullptr, 0);
+                                                           nullptr, 0, nullptr, nullptr, 0, a.extra);
   else
     combine_kernel<true, false><<<grid, 256, 0, stream>>>(a.partial, a.out, a.T, a.N, a.k, a.slot,
-                                                          a.num_slots, a.cache, nullptr, 0);
+                                                          a.num_slots, a.cache, nullptr, 0, a.extra);
   return hipGetLastError();
 }
 

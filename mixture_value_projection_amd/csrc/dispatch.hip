@@ -24,19 +24,20 @@
 namespace mova {
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanWaves = kScanThreads / 64;
+constexpr int kScanCols = kMaxDispatchExperts;              // one thread per expert
+constexpr int kScanGroups = kScanThreads / kScanCols;       // chunk ranges
 
-// One workgroup; lane = expert, so every count load is a contiguous row of
-// the [C, E] table.  Wave w owns chunks [w * per, (w + 1) * per).
+// One workgroup; thread column = expert, so every count load is a contiguous
+// row of the [C, E] table.  Group w owns chunks [w * per, (w + 1) * per).
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     int32_t* __restrict__ counts, int C, int E, int block_m,
     int32_t* __restrict__ expert_off, int32_t* __restrict__ tile_base) {
-  __shared__ int wave_sum[kScanWaves][kMaxExperts];
-  __shared__ int total[kMaxExperts];
-  __shared__ int mtiles[kMaxExperts];
-  const int e = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int per = ceil_div(C, kScanWaves);
+  __shared__ int wave_sum[kScanGroups][kScanCols];
+  __shared__ int total[kScanCols];
+  __shared__ int mtiles[kScanCols];
+  const int e = threadIdx.x % kScanCols;
+  const int w = threadIdx.x / kScanCols;
+  const int per = ceil_div(C, kScanGroups);
   const int c0 = min(C, w * per), c1 = min(C, c0 + per);
   const bool live = e < E;
 
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   __syncthreads();
   int run = 0;
   for (int i = 0; i < w; ++i) run += wave_sum[i][e];
-  if (w == kScanWaves - 1) {
+  if (w == kScanGroups - 1) {
     total[e] = live ? run + s : 0;
     mtiles[e] = live ? ceil_div(run + s, block_m) : 0;
   }
@@ -73,11 +74,11 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   }
   __syncthreads();
   if (w == 0) {
-    // Expert offsets and first M-tiles: lane e sums the experts before it
+    // Expert offsets and first M-tiles: thread e sums the experts before it
     // (entries past E are zero).
     int off = 0, tiles = 0, all = 0, all_tiles = 0;
 #pragma unroll 16
-    for (int i = 0; i < kMaxExperts; ++i) {
+    for (int i = 0; i < kScanCols; ++i) {
       const int t = total[i];
       const int mt = mtiles[i];
       off += i < e ? t : 0;
@@ -100,16 +101,16 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ chunk_off,
     const int32_t* __restrict__ expert_off, int32_t* __restrict__ perm,
     int T, int E, int k, int chunk_tokens) {
-  __shared__ int running[kMaxExperts];
-  __shared__ int wave_cnt[4][kMaxExperts];
+  __shared__ int running[kMaxDispatchExperts];
+  __shared__ int wave_cnt[4][kMaxDispatchExperts];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c = blockIdx.x;
   const int p0 = c * chunk_tokens * k;
   const int npairs = min(T * k, p0 + chunk_tokens * k) - p0;
 
-  if (threadIdx.x < kMaxExperts) running[threadIdx.x] = 0;
-  for (int i = threadIdx.x; i < 4 * kMaxExperts; i += 256) (&wave_cnt[0][0])[i] = 0;
+  if (threadIdx.x < kMaxDispatchExperts) running[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < 4 * kMaxDispatchExperts; i += 256) (&wave_cnt[0][0])[i] = 0;
   __syncthreads();
 
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -118,10 +119,10 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const int e_raw = p < npairs ? idx[p0 + p] : 0;
     const bool valid = p < npairs && e_raw >= 0 && e_raw < E;
     const int e = valid ? e_raw : 0;
-    // Lanes of this wave holding the same expert (6 ballots over the id bits).
+    // Lanes of this wave holding the same expert (7 ballots over the id bits).
     uint64_t peers = __ballot(valid);
 #pragma unroll
-    for (int b = 0; b < 6; ++b) {
+    for (int b = 0; b < 7; ++b) {
       const bool bit = (e >> b) & 1;
       const uint64_t on = __ballot(bit);
       peers &= bit ? on : ~on;
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
       perm[expert_off[e] + chunk_off[(size_t)c * E + e] + rank] = p0 + p;
     }
     __syncthreads();
-    if (threadIdx.x < kMaxExperts) {
+    if (threadIdx.x < kMaxDispatchExperts) {
       const int x = threadIdx.x;
       running[x] += wave_cnt[0][x] + wave_cnt[1][x] + wave_cnt[2][x] + wave_cnt[3][x];
       wave_cnt[0][x] = wave_cnt[1][x] = wave_cnt[2][x] = wave_cnt[3][x] = 0;
@@ -149,11 +150,11 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx,
                                                              int32_t* __restrict__ counts, int T,
                                                              int E, int k, int chunk_tokens) {
-  __shared__ int hist[kMaxExperts];
+  __shared__ int hist[kMaxDispatchExperts];
   const int c = blockIdx.x;
   const int p0 = c * chunk_tokens * k;
   const int npairs = min(T * k, p0 + chunk_tokens * k) - p0;
-  if (threadIdx.x < kMaxExperts) hist[threadIdx.x] = 0;
+  if (threadIdx.x < kMaxDispatchExperts) hist[threadIdx.x] = 0;
   __syncthreads();
   for (int p = threadIdx.x; p < npairs; p += 256) {
     const int e = idx[p0 + p];

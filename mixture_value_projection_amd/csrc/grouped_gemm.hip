@@ -166,17 +166,37 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[kBM / kWM / 16][kBN / kWN 
   }
 }
 
-// kDense = false: grouped mode (perm, topk_w, expert_off, tile_base, partial).
-// kDense = true: dense mode over T token rows and one [N, d] weight (out).
-template <MOVA_TILE_PARAMS, bool kDense>
+constexpr bool mode_routed(int m) {
+  return m == kGemmRoutedSilu || m == kGemmRoutedSwiGLU || m == kGemmRoutedLinear;
+}
+constexpr bool mode_swiglu(int m) { return m == kGemmRoutedSwiGLU || m == kGemmDenseSwiGLU; }
+
+// Routed modes: tiles over the experts' pair rows (perm, expert_off,
+// tile_base), B = W[e].  Dense modes: tiles over T rows in order, B = W (one
+// [N, d] weight).  A rows: token perm[r] / k of x (routed SiLU / SwiGLU),
+// row perm[r] of x (routed linear: x holds one row per pair), or row r
+// (dense).  Epilogues (kGemm* in kernels.h):
+//   RoutedSilu    partial[pair, n] = fp16(w * SiLU(z))
+//   Dense         out[r, n]        = bf16(z)
+//   RoutedSwiGLU  out[pair, c]     = bf16(SiLU(z_gate) * z_up)
+//   RoutedLinear  partial[pair, n] = fp16(w * z)
+//   DenseSwiGLU   out[r, c]        = bf16(SiLU(z_gate) * z_up)
+//   DenseF16      partial[r, n]    = fp16(z)
+// SwiGLU weights interleave gate and up rows in blocks of 16: rows 32b .. 32b+15
+// are gate rows 16b .. 16b+15 and rows 32b+16 .. 32b+31 the matching up rows,
+// so the wave's column tiles 2j and 2j+1 hold the gate and up values of the
+// same 16 outputs c = (column of tile 2j) / 2 .. + 15; out has N / 2 columns.
+template <MOVA_TILE_PARAMS, int kMode>
 __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ perm, const float* __restrict__ topk_w,
     const int32_t* __restrict__ expert_off, const int32_t* __restrict__ tile_base,
     f16_t* __restrict__ partial, bf16_t* __restrict__ out, int T, int d, int N, int E, int k) {
   using TL = Tile<MOVA_TILE_ARGS>;
+  constexpr bool kDense = !mode_routed(kMode);
   constexpr int WN = TL::kColsW;  // columns per wave
-  extern __shared__ __attribute__((aligned(1024))) char smem[];  // 2 stages
+  static_assert(!mode_swiglu(kMode) || WN % 32 == 0, "SwiGLU pairs 16-column tiles");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];  // kS stages
   __shared__ int tile_pair[kDense ? 1 : kBM];
   __shared__ float tile_w[kDense ? 1 : kBM];
 
@@ -216,11 +236,11 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
   const int wm = wave / kWN, wn = wave % kWN;
   const int q = lane >> 4, r16 = lane & 15;
 
-  if (!kDense) {
+  if constexpr (!kDense) {
     for (int r = tid; r < kBM; r += TL::kThreads) {
       const int pair = perm[row0 + min(r, rows - 1)];
       tile_pair[r] = pair;
-      tile_w[r] = topk_w[pair];
+      tile_w[r] = kMode == kGemmRoutedSwiGLU ? 0.f : topk_w[pair];
     }
   }
 
@@ -234,8 +254,10 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     const int row = (wave * TL::kLoadsA + i) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ (row & 7);
     const int rr = row0 + min(row, rows - 1);
-    const int token = kDense ? rr : perm[rr] / k;
-    c.a_src[i] = reinterpret_cast<const char*>(x + (size_t)token * d) + chunk * 16;
+    int arow = rr;
+    if constexpr (kMode == kGemmRoutedLinear) arow = perm[rr];
+    else if constexpr (!kDense) arow = perm[rr] / k;
+    c.a_src[i] = reinterpret_cast<const char*>(x + (size_t)arow * d) + chunk * 16;
   }
 #pragma unroll
   for (int i = 0; i < TL::kLoadsB; ++i) {
@@ -302,35 +324,47 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     if (!active) return;
   }
 
-  // Epilogue.  Grouped: y = w * SiLU(z) into the pair's partial row (fp16).
-  // Dense: z into the token's output row (bf16).
+  // Epilogue (see the mode table above).
+  const int cb = n0 + wn * WN;  // first column of the wave's sub-tile
 #pragma unroll
   for (int i = 0; i < TL::kMI; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int r = wm * TL::kRowsW + i * 16 + q * 4 + v;
       if (r < rows) {
-        if (kDense) {
-          bf16_t* dst = out + (size_t)(row0 + r) * N + n0 + wn * WN + r16;
+        const size_t orow = kDense ? (size_t)(row0 + r) : (size_t)tile_pair[r];
+        if constexpr (mode_swiglu(kMode)) {
+          bf16_t* dst = out + orow * (N / 2) + cb / 2 + r16;
+#pragma unroll
+          for (int j = 0; j < TL::kNJ; j += 2)
+            if (cb + j * 16 + r16 < N)
+              dst[j * 8] = (bf16_t)(siluf(acc[i][j][v]) * acc[i][j + 1][v]);
+        } else if constexpr (kMode == kGemmDense) {
+          bf16_t* dst = out + orow * N + cb + r16;
 #pragma unroll
           for (int j = 0; j < TL::kNJ; ++j)
-            if (n0 + wn * WN + j * 16 + r16 < N) dst[j * 16] = (bf16_t)acc[i][j][v];
+            if (cb + j * 16 + r16 < N) dst[j * 16] = (bf16_t)acc[i][j][v];
         } else {
-          const int pair = tile_pair[r];
-          const float wt = tile_w[r];
-          f16_t* dst = partial + (size_t)pair * N + n0 + wn * WN + r16;
+          f16_t* dst = partial + orow * N + cb + r16;
+          const float wt = kDense ? 1.f : tile_w[r];
 #pragma unroll
-          for (int j = 0; j < TL::kNJ; ++j)
-            if (n0 + wn * WN + j * 16 + r16 < N) dst[j * 16] = (f16_t)(wt * siluf(acc[i][j][v]));
+          for (int j = 0; j < TL::kNJ; ++j) {
+            if (cb + j * 16 + r16 < N) {
+              const float z = acc[i][j][v];
+              if constexpr (kMode == kGemmRoutedSilu) dst[j * 16] = (f16_t)(wt * siluf(z));
+              else if constexpr (kMode == kGemmRoutedLinear) dst[j * 16] = (f16_t)(wt * z);
+              else dst[j * 16] = (f16_t)z;
+            }
+          }
         }
       }
     }
   }
 }
 
-template <MOVA_TILE_PARAMS, bool kDense>
+template <MOVA_TILE_PARAMS, int kMode>
 hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) {
-  auto kern = gemm_kernel<MOVA_TILE_ARGS, kDense>;
+  auto kern = gemm_kernel<MOVA_TILE_ARGS, kMode>;
   constexpr int smem = kS * Tile<MOVA_TILE_ARGS>::kStage;
   constexpr int threads = Tile<MOVA_TILE_ARGS>::kThreads;
   static bool attr_set = false;
@@ -347,18 +381,29 @@ hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) 
   return hipGetLastError();
 }
 
+template <int kMode>
+static hipError_t launch_routed_mode(const GemmArgs& a, long long ub, hipStream_t stream) {
+  const GemmTile t = a.tile;
+  if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, kMode>(a, ub, stream);
+  if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, kMode>(a, ub, stream);
+  if (t.bm == 128 && t.bn == 128 && t.waves == 8) {
+    if (t.stages == 3) return launch_tiles<128, 128, 2, 4, 3, kMode>(a, ub, stream);
+    if (t.stages == 4) return launch_tiles<128, 128, 2, 4, 4, kMode>(a, ub, stream);
+    return launch_tiles<128, 128, 2, 4, 2, kMode>(a, ub, stream);
+  }
+  if (t.bm == 128 && t.bn == 128) return launch_tiles<128, 128, 2, 2, 4, kMode>(a, ub, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   const GemmTile t = a.tile;
   const long long ub = (long long)gemm_max_mtiles(a.T, a.k, a.E, t.bm) * ceil_div(a.N, t.bn);
-  if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, false>(a, ub, stream);
-  if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, false>(a, ub, stream);
-  if (t.bm == 128 && t.bn == 128 && t.waves == 8) {
-    if (t.stages == 3) return launch_tiles<128, 128, 2, 4, 3, false>(a, ub, stream);
-    if (t.stages == 4) return launch_tiles<128, 128, 2, 4, 4, false>(a, ub, stream);
-    return launch_tiles<128, 128, 2, 4, 2, false>(a, ub, stream);
+  switch (a.mode) {
+    case kGemmRoutedSilu: return launch_routed_mode<kGemmRoutedSilu>(a, ub, stream);
+    case kGemmRoutedSwiGLU: return launch_routed_mode<kGemmRoutedSwiGLU>(a, ub, stream);
+    case kGemmRoutedLinear: return launch_routed_mode<kGemmRoutedLinear>(a, ub, stream);
+    default: return hipErrorInvalidValue;
   }
-  if (t.bm == 128 && t.bn == 128) return launch_tiles<128, 128, 2, 2, 4, false>(a, ub, stream);
-  return hipErrorInvalidValue;
 }
 
 GemmTile gemm_tile_dense(int T, int N) {
@@ -373,17 +418,28 @@ GemmTile gemm_tile_dense(int T, int N) {
   return {128, 128, 8, 2};
 }
 
+template <int kMode>
+static hipError_t launch_dense_mode(const GemmArgs& a, GemmTile t, long long tiles,
+                                    hipStream_t stream) {
+  if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, kMode>(a, tiles, stream);
+  if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, kMode>(a, tiles, stream);
+  if (t.waves == 8) {
+    if (t.stages == 3) return launch_tiles<128, 128, 2, 4, 3, kMode>(a, tiles, stream);
+    if (t.stages == 4) return launch_tiles<128, 128, 2, 4, 4, kMode>(a, tiles, stream);
+    return launch_tiles<128, 128, 2, 4, 2, kMode>(a, tiles, stream);
+  }
+  return launch_tiles<128, 128, 2, 2, 4, kMode>(a, tiles, stream);
+}
+
 hipError_t launch_dense_gemm(const GemmArgs& a, hipStream_t stream) {
   const GemmTile t = gemm_tile_dense(a.T, a.N);
   const long long tiles = (long long)ceil_div(a.T, t.bm) * ceil_div(a.N, t.bn);
-  if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, true>(a, tiles, stream);
-  if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, true>(a, tiles, stream);
-  if (t.waves == 8) {
-    if (t.stages == 3) return launch_tiles<128, 128, 2, 4, 3, true>(a, tiles, stream);
-    if (t.stages == 4) return launch_tiles<128, 128, 2, 4, 4, true>(a, tiles, stream);
-    return launch_tiles<128, 128, 2, 4, 2, true>(a, tiles, stream);
+  switch (a.mode) {
+    case kGemmDense: return launch_dense_mode<kGemmDense>(a, t, tiles, stream);
+    case kGemmDenseSwiGLU: return launch_dense_mode<kGemmDenseSwiGLU>(a, t, tiles, stream);
+    case kGemmDenseF16: return launch_dense_mode<kGemmDenseF16>(a, t, tiles, stream);
+    default: return hipErrorInvalidValue;
   }
-  return launch_tiles<128, 128, 2, 2, 4, true>(a, tiles, stream);
 }
 
 }  // namespace mova

@@ -29,6 +29,10 @@ hipError_t launch_router_tile(const RouterArgs& a, hipStream_t stream);
 int router_small_plog_floats(int T);
 hipError_t launch_router_small(const RouterArgs& a, float* plog, hipStream_t stream);
 
+// Experts the dispatch kernels handle (the value router itself takes at most
+// kMaxExperts; routing of wider layers comes from their own router).
+constexpr int kMaxDispatchExperts = 128;
+
 struct DispatchArgs {
   const int32_t* idx;     // [T, k] routing
   int32_t* chunk_counts;  // [C, E] in: per-chunk counts; out: per-chunk offsets
@@ -51,17 +55,28 @@ struct GemmTile {
   int bm, bn, waves, stages;
 };
 
+// What the tiled GEMM computes (epilogues in grouped_gemm.hip).
+enum GemmMode {
+  kGemmRoutedSilu = 0,    // value experts: partial = w * SiLU(x W_e^T), fp16
+  kGemmDense = 1,         // dense v_proj: out = x W^T, bf16
+  kGemmRoutedSwiGLU = 2,  // FFN experts, gate/up: out[pair] = SiLU(gate) * up, bf16
+  kGemmRoutedLinear = 3,  // FFN experts, down: partial = w * (h_pair W_e^T), fp16
+  kGemmDenseSwiGLU = 4,   // shared FFN expert, gate/up, bf16
+  kGemmDenseF16 = 5       // shared FFN expert, down: partial = x W^T, fp16
+};
+
 struct GemmArgs {
-  const __bf16* x;         // [T, d]
-  const __bf16* W;         // [E, N, d]
+  const __bf16* x;         // A rows: [T, d] (or [T * k, d] for kGemmRoutedLinear)
+  const __bf16* W;         // [E, N, d] (dense modes: [N, d])
   const int32_t* perm;     // [T * k]
   const float* topk_w;     // [T * k]
   const int32_t* expert_off;
-  const int32_t* tile_base;  // M-tile bases for tile.bm (grouped mode)
-  f16_t* partial;          // [T * k, N] (grouped mode)
-  __bf16* out;             // [T, N] (dense mode)
+  const int32_t* tile_base;  // M-tile bases for tile.bm (routed modes)
+  f16_t* partial;          // fp16 results ([T * k, N] routed, [T, N] dense)
+  __bf16* out;             // bf16 results ([T, N], or [T * k or T, N / 2] SwiGLU)
   int T, d, N, E, k;
-  GemmTile tile;           // grouped mode; dense mode chooses its own
+  GemmTile tile;           // routed modes; dense modes choose their own
+  int mode = kGemmRoutedSilu;
 };
 // Tile of the grouped GEMM for a call (the dispatch builds M-tiles of tile.bm rows).
 GemmTile gemm_tile_grouped(int T, int k, int E);
@@ -112,7 +127,17 @@ struct CombineArgs {
   // written).
   const int32_t* idx = nullptr;
   int E = 0;
+  // Optional [T, N] fp16 term added after the k slots (the FFN's shared expert).
+  const f16_t* extra = nullptr;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// FFN mixture of experts (ffn.hip): router for E <= kMaxDispatchExperts (one
+// workgroup per ffn_router_chunk_tokens() tokens, which is also the dispatch
+// chunk; chunk_counts [blocks, E]), and the gate/up row interleaving.
+int ffn_router_chunk_tokens();
+hipError_t launch_ffn_router(const RouterArgs& a, hipStream_t stream);
+hipError_t launch_ffn_pack_gate_up(const __bf16* gate, const __bf16* up, __bf16* dst, int E,
+                                   int inter, int d, hipStream_t stream);
 
 }  // namespace mova

@@ -109,6 +109,48 @@ size_t dense_workspace(int T, int d, int N) {
   return T <= kDenseSkinnyMaxT ? align256(dense_skinny_partial_floats(T, d, N) * 4) : 0;
 }
 
+// FFN mixture of experts (mova_ffn_moe_forward).  Domain: 1 <= E <= 128,
+// 1 <= k <= min(E, 8), d % 64 == 0 and d <= 16384 (d is also the output
+// width), inter % 64 == 0 and 0 < inter <= 16384, inter_shared == 0 (no
+// shared expert) or as inter.
+int check_ffn(int T, int d, int E, int k, int inter, int inter_shared) {
+  if (T < 0 || d <= 0 || E <= 0 || k <= 0 || inter <= 0 || inter_shared < 0)
+    return MOVA_ERR_INVALID_ARG;
+  if (T > kMaxT || E > kMaxDispatchExperts || k > kMaxTopK || k > E) return MOVA_ERR_UNSUPPORTED;
+  if (d % 64 != 0 || d > (1 << 14) || inter % 64 != 0 || inter > (1 << 14))
+    return MOVA_ERR_UNSUPPORTED;
+  if (inter_shared % 64 != 0 || inter_shared > (1 << 14)) return MOVA_ERR_UNSUPPORTED;
+  return MOVA_OK;
+}
+
+// FFN workspace (every region 256-byte aligned):
+//   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] |
+//   tile_base [E+1] | perm [T*k] i32 | h [T*k, inter] bf16 | partial [T*k, d] f16 |
+//   shared h [T, inter_shared] bf16 | shared partial [T, d] f16
+// C = ceil(T / ffn_router_chunk_tokens()).
+struct FfnLayout {
+  size_t idx, w, chunk, eoff, tbase, perm, h, partial, hs, ps, total;
+};
+
+FfnLayout ffn_layout(int T, int d, int E, int k, int inter, int inter_shared) {
+  const size_t pairs = (size_t)T * k;
+  const size_t C = (size_t)ceil_div(T, ffn_router_chunk_tokens());
+  FfnLayout L;
+  size_t o = 0;
+  L.idx = o;     o += align256(pairs * 4);
+  L.w = o;       o += align256(pairs * 4);
+  L.chunk = o;   o += align256(C * E * 4);
+  L.eoff = o;    o += align256((size_t)(E + 1) * 4);
+  L.tbase = o;   o += align256((size_t)(E + 1) * 4);
+  L.perm = o;    o += align256(pairs * 4);
+  L.h = o;       o += align256(pairs * inter * 2);
+  L.partial = o; o += align256(pairs * d * 2);
+  L.hs = o;      o += align256((size_t)T * inter_shared * 2);
+  L.ps = o;      o += align256(inter_shared > 0 ? (size_t)T * d * 2 : 0);
+  L.total = o;
+  return L;
+}
+
 // ---- stage timing -------------------------------------------------------
 constexpr int kStages = 5;
 struct Timing {
@@ -351,8 +393,110 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
   } else {
     StageScope sc(4, stream);
     GemmArgs ga{(const __bf16*)x, (const __bf16*)w_v, nullptr, nullptr, nullptr, nullptr,
-                nullptr, (__bf16*)out, T, d, N, 1, 1, {0, 0, 0, 0}};
+                nullptr, (__bf16*)out, T, d, N, 1, 1, {0, 0, 0, 0}, kGemmDense};
     err = launch_dense_gemm(ga, stream);
+  }
+  return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+}
+
+size_t mova_ffn_workspace_bytes(int T, int d, int E, int k, int inter, int inter_shared) {
+  if (check_ffn(T, d, E, k, inter, inter_shared) != MOVA_OK) return (size_t)-1;
+  if (T == 0) return 0;
+  return ffn_layout(T, d, E, k, inter, inter_shared).total;
+}
+
+int mova_ffn_pack_gate_up(const void* gate_w, const void* up_w, int E, int inter, int d,
+                          void* gate_up_w, hipStream_t stream) {
+  if (E <= 0 || inter <= 0 || d <= 0) return MOVA_ERR_INVALID_ARG;
+  if (E > kMaxDispatchExperts || inter % 64 != 0 || inter > (1 << 14) || d % 64 != 0 ||
+      d > (1 << 14))
+    return MOVA_ERR_UNSUPPORTED;
+  if (gate_w == nullptr || up_w == nullptr || gate_up_w == nullptr) return MOVA_ERR_INVALID_ARG;
+  if (!aligned16(gate_w) || !aligned16(up_w) || !aligned16(gate_up_w)) return MOVA_ERR_INVALID_ARG;
+  return launch_ffn_pack_gate_up((const __bf16*)gate_w, (const __bf16*)up_w, (__bf16*)gate_up_w, E,
+                                 inter, d, stream) == hipSuccess
+             ? MOVA_OK
+             : MOVA_ERR_HIP;
+}
+
+int mova_ffn_moe_forward(const void* x, const void* router_w, const float* router_b,
+                         const void* gate_up_w, const void* down_w, int E, int k, int inter,
+                         const void* shared_gate_up_w, const void* shared_down_w,
+                         int inter_shared, int T, int d, float scale, void* out,
+                         int32_t* topk_idx_out, float* topk_w_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_ffn(T, d, E, k, inter, inter_shared);
+  if (rc != MOVA_OK) return rc;
+  if (!isfinite(scale)) return MOVA_ERR_UNSUPPORTED;
+  if (T == 0) return MOVA_OK;
+  if (x == nullptr || router_w == nullptr || gate_up_w == nullptr || down_w == nullptr ||
+      out == nullptr)
+    return MOVA_ERR_INVALID_ARG;
+  if (inter_shared > 0 && (shared_gate_up_w == nullptr || shared_down_w == nullptr))
+    return MOVA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(router_w) || !aligned16(router_b) || !aligned16(gate_up_w) ||
+      !aligned16(down_w) || !aligned16(shared_gate_up_w) || !aligned16(shared_down_w) ||
+      !aligned16(out) || !aligned16(topk_idx_out) || !aligned16(topk_w_out))
+    return MOVA_ERR_INVALID_ARG;
+  const FfnLayout L = ffn_layout(T, d, E, k, inter, inter_shared);
+  if (workspace == nullptr || workspace_bytes < L.total) return MOVA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOVA_ERR_INVALID_ARG;
+
+  char* ws = (char*)workspace;
+  int32_t* idx = topk_idx_out ? topk_idx_out : (int32_t*)(ws + L.idx);
+  float* w = topk_w_out ? topk_w_out : (float*)(ws + L.w);
+  int32_t* chunk = (int32_t*)(ws + L.chunk);
+  int32_t* eoff = (int32_t*)(ws + L.eoff);
+  int32_t* tbase = (int32_t*)(ws + L.tbase);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  __bf16* h = (__bf16*)(ws + L.h);
+  f16_t* partial = (f16_t*)(ws + L.partial);
+  __bf16* hs = (__bf16*)(ws + L.hs);
+  f16_t* ps = (f16_t*)(ws + L.ps);
+  const __bf16* xb = (const __bf16*)x;
+  hipError_t err;
+  {
+    StageScope sc(0, stream);
+    RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w, chunk};
+    err = launch_ffn_router(ra, stream);
+  }
+  if (err != hipSuccess) return MOVA_ERR_HIP;
+  const GemmTile tile = gemm_tile_grouped(T, k, E);
+  {
+    StageScope sc(1, stream);
+    DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, ffn_router_chunk_tokens(), tile.bm};
+    err = launch_dispatch(dp, stream);
+  }
+  if (err != hipSuccess) return MOVA_ERR_HIP;
+  {
+    StageScope sc(2, stream);
+    // Routed experts: h[pair] = SiLU(gate x) * (up x), then partial[pair] =
+    // w * (down h); the shared expert the same on every token, unweighted.
+    GemmArgs gu{xb, (const __bf16*)gate_up_w, perm, w, eoff, tbase, nullptr, h,
+                T, d, 2 * inter, E, k, tile, kGemmRoutedSwiGLU};
+    err = launch_grouped_gemm(gu, stream);
+    if (err == hipSuccess) {
+      GemmArgs dn{h, (const __bf16*)down_w, perm, w, eoff, tbase, partial, nullptr,
+                  T, inter, d, E, k, tile, kGemmRoutedLinear};
+      err = launch_grouped_gemm(dn, stream);
+    }
+    if (err == hipSuccess && inter_shared > 0) {
+      GemmArgs sg{xb, (const __bf16*)shared_gate_up_w, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, hs, T, d, 2 * inter_shared, 1, 1, {0, 0, 0, 0}, kGemmDenseSwiGLU};
+      err = launch_dense_gemm(sg, stream);
+      if (err == hipSuccess) {
+        GemmArgs sd{hs, (const __bf16*)shared_down_w, nullptr, nullptr, nullptr, nullptr, ps,
+                    nullptr, T, inter_shared, d, 1, 1, {0, 0, 0, 0}, kGemmDenseF16};
+        err = launch_dense_gemm(sd, stream);
+      }
+    }
+  }
+  if (err != hipSuccess) return MOVA_ERR_HIP;
+  {
+    StageScope sc(3, stream);
+    CombineArgs ca{partial, (__bf16*)out, T, d, k};
+    ca.extra = inter_shared > 0 ? ps : nullptr;
+    err = launch_combine(ca, stream);
   }
   return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }

@@ -45,6 +45,9 @@ __all__ = [
     "make_weights",
     "make_dense_vproj",
     "make_workload",
+    "FfnShape",
+    "FFN_WORKLOADS",
+    "make_ffn_layer",
 ]
 
 # Zipf exponent of the skewed-routing workload, and the scale of the bias that
@@ -209,3 +212,55 @@ def make_workload(name: str, layer: int = 0, T: Optional[int] = None) -> Dict[st
     w = WORKLOADS[name]
     shape = w.shape if T is None else dataclasses.replace(w.shape, T=T)
     return make_layer(shape, w.seed, w.dtype, w.bias, layer)
+
+
+# ---------------------------------------------------------------- FFN MoE
+
+@dataclasses.dataclass(frozen=True)
+class FfnShape:
+    """Sizes of one FFN mixture-of-experts layer: T tokens of width d, E SwiGLU
+    experts of intermediate width ``inter`` (k per token) and a shared expert
+    of width ``inter_shared`` (0 = none)."""
+
+    T: int
+    d: int
+    E: int
+    k: int
+    inter: int
+    inter_shared: int
+    scale: float = 2.5
+
+
+# The pages give 100 experts with top-8 routing plus one shared expert, but no
+# expert width; 768 makes the model's parameter count come out at the page's
+# total (see the design notes) and is used for both expert kinds.
+_FFN = dict(d=2560, E=100, k=8, inter=768, inter_shared=768)
+
+FFN_WORKLOADS: Dict[str, FfnShape] = {
+    "ffn_decode": FfnShape(T=64, **_FFN),
+    "ffn_prefill": FfnShape(T=4096, **_FFN),
+}
+
+
+def make_ffn_layer(shape: FfnShape, seed: int = 0,
+                   dtype: torch.dtype = torch.bfloat16) -> Dict[str, torch.Tensor]:
+    """x [T, d] ~ N(0, 1); router W [E, d] ~ N(0, 0.02), bias ~ U(-0.01, 0.01);
+    gate / up [E, inter, d] ~ N(0, 1/sqrt(d)); down [E, d, inter] ~
+    N(0, 1/sqrt(inter)); the shared expert's three matrices likewise.
+    Sub-seeds seed + 10 .. seed + 17.  CPU tensors (bias fp32)."""
+    T, d, E, I, Is = shape.T, shape.d, shape.E, shape.inter, shape.inter_shared
+    out = {
+        "x": _round(torch.randn(T, d, generator=_gen(seed + 10)), dtype),
+        "router_w": _round(torch.randn(E, d, generator=_gen(seed + 11)) * 0.02, dtype),
+        "router_b": (torch.rand(E, generator=_gen(seed + 12)) * 0.02 - 0.01).to(torch.float32),
+        "gate_w": _round(torch.randn(E, I, d, generator=_gen(seed + 13)) / math.sqrt(d), dtype),
+        "up_w": _round(torch.randn(E, I, d, generator=_gen(seed + 14)) / math.sqrt(d), dtype),
+        "down_w": _round(torch.randn(E, d, I, generator=_gen(seed + 15)) / math.sqrt(I), dtype),
+    }
+    if Is > 0:
+        g = _gen(seed + 16)
+        out["shared_gate_w"] = _round(torch.randn(Is, d, generator=g) / math.sqrt(d), dtype)
+        out["shared_up_w"] = _round(torch.randn(Is, d, generator=g) / math.sqrt(d), dtype)
+        out["shared_down_w"] = _round(torch.randn(d, Is, generator=_gen(seed + 17)) / math.sqrt(Is),
+                                      dtype)
+    return out

@@ -12,8 +12,9 @@ Parity status per function (details in the module docstring of
 * ``router_logits``, ``sigmoid``, ``route`` (except the bias role and the
   router's reduction order), ``combine_experts``, ``value_forward`` and
   ``dense_value_proj`` (the matched dense baseline) and
-  ``paged_value_write`` (the paged cache store) and ``rebuild_values`` (the
-  compact cache's reconstruction): pinned by the tests in
+  ``paged_value_write`` (the paged cache store), ``rebuild_values`` (the
+  compact cache's reconstruction), ``swiglu_expert`` and ``ffn_moe_forward``
+  (the FFN mixture of experts): pinned by the tests in
   ``tests/test_oracle_pins.py``;
 * the role of the router bias (added to the scores for selection only) and
   the router's summation order: parity unpinned -- no page prints a value
@@ -24,6 +25,8 @@ from .mova_oracle import (  # noqa: F401
     Routing,
     combine_experts,
     dense_value_proj,
+    ffn_moe_forward,
+    swiglu_expert,
     paged_value_write,
     rebuild_values,
     route,

@@ -227,3 +227,37 @@ def rebuild_values(x, expert_w, idx, w) -> np.ndarray:
             z = W[e] @ x[t]
             out[t] += w[t, j] * silu(z)
     return out
+
+
+def swiglu_expert(x, gate_w, up_w, down_w) -> np.ndarray:
+    """One SwiGLU FFN expert, down( SiLU(gate x) * (up x) ), bias-free,
+    nn.Linear weight layout ([out, in]).  Rows of x are tokens."""
+    x = _f64(x)
+    g = x @ _f64(gate_w).T
+    u = x @ _f64(up_w).T
+    return (silu(g) * u) @ _f64(down_w).T
+
+
+def ffn_moe_forward(x, router_w, router_b, gate_w, up_w, down_w, k: int, scale: float,
+                    shared=None):
+    """FFN mixture of experts with top-k routing plus an optional shared
+    expert (the thevalue.engineering page on the MoVA architecture, section
+    "Dual sparsity": 100 FFN experts, top-8+1).  The pages fix neither the
+    expert shape nor the routing function.  Readings: SwiGLU experts
+    (``swiglu_expert``); routing by the value router's function (``route``:
+    sigmoid scores, bias for selection, renormalised top-k times ``scale``);
+    out = sum_j w_j expert_{idx_j}(x) + shared(x), with ``shared`` a
+    (gate_w, up_w, down_w) triple or None.  Returns (out [T, d] float64,
+    Routing).
+    """
+    x = _f64(x)
+    r = route(x, router_w, router_b, k, scale)
+    G, U, D = _f64(gate_w), _f64(up_w), _f64(down_w)
+    out = np.zeros((x.shape[0], D.shape[1]))
+    for t in range(x.shape[0]):
+        for j in range(k):
+            e = int(r.idx[t, j])
+            out[t] += r.w[t, j] * swiglu_expert(x[t:t + 1], G[e], U[e], D[e])[0]
+    if shared is not None:
+        out += swiglu_expert(x, *shared)
+    return out, r

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     for n in ("mova_route", "mova_value_forward", "mova_workspace_bytes", "mova_status_str",
               "mova_version", "mova_timing_enable", "mova_timing_read",
               "mova_dense_value_proj", "mova_dense_workspace_bytes",
-              "mova_value_forward_paged", "mova_value_from_routing"):
+              "mova_value_forward_paged", "mova_value_from_routing", "mova_ffn_moe_forward",
+              "mova_ffn_workspace_bytes", "mova_ffn_pack_gate_up"):
         assert n in names
 
 
@@ -169,6 +170,54 @@ def test_rebuild_rejects(lib, kw, rc):
 
 def test_rebuild_empty_is_noop(lib):
     assert rebuild(lib, T=0, x=None, idx=None, w=None, out=None, ws=None, wsb=0) == OK
+
+
+def test_ffn_workspace_bytes(lib):
+    assert binding.ffn_workspace_bytes(0, 2560, 100, 8, 768, 768) == 0
+    n = binding.ffn_workspace_bytes(64, 2560, 100, 8, 768, 768)
+    assert n % 256 == 0 and n >= 64 * 8 * (768 * 2 + 2560 * 2) + 64 * 2560 * 2
+    bad = ctypes.c_size_t(-1).value
+    assert lib.mova_ffn_workspace_bytes(16, 2560, 129, 8, 768, 0) == bad   # E > 128
+    assert lib.mova_ffn_workspace_bytes(16, 2560, 100, 9, 768, 0) == bad   # k > 8
+    assert lib.mova_ffn_workspace_bytes(16, 2500, 100, 8, 768, 0) == bad   # d % 64
+    assert lib.mova_ffn_workspace_bytes(16, 2560, 100, 8, 700, 0) == bad   # inter % 64
+    assert lib.mova_ffn_workspace_bytes(16, 2560, 100, 8, 768, 100) == bad  # shared % 64
+
+
+def ffn(lib, **kw):
+    a = dict(x=FAKE, rw=FAKE, rb=None, gu=FAKE, dn=FAKE, E=100, k=8, I=128, sgu=None, sdn=None,
+             Is=0, T=16, d=256, scale=2.5, out=FAKE, idx=None, w=None, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(kw)
+    return lib.mova_ffn_moe_forward(a["x"], a["rw"], a["rb"], a["gu"], a["dn"], a["E"], a["k"],
+                                    a["I"], a["sgu"], a["sdn"], a["Is"], a["T"], a["d"], a["scale"],
+                                    a["out"], a["idx"], a["w"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(T=-1), INVALID), (dict(E=0), INVALID), (dict(E=129), UNSUPPORTED),
+    (dict(k=9), UNSUPPORTED), (dict(k=5, E=4), UNSUPPORTED), (dict(d=100), UNSUPPORTED),
+    (dict(I=96), UNSUPPORTED), (dict(I=0), INVALID), (dict(Is=64), INVALID),
+    (dict(Is=64, sgu=FAKE, sdn=FAKE + 4), INVALID), (dict(scale=float("nan")), UNSUPPORTED),
+    (dict(x=None), INVALID), (dict(gu=None), INVALID), (dict(dn=None), INVALID),
+    (dict(out=None), INVALID), (dict(out=FAKE + 2), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(wsb=1024), WORKSPACE), (dict(ws=FAKE + 16), INVALID),
+])
+def test_ffn_rejects(lib, kw, rc):
+    assert ffn(lib, **kw) == rc
+
+
+def test_ffn_empty_is_noop(lib):
+    assert ffn(lib, T=0, x=None, out=None, ws=None, wsb=0) == OK
+
+
+@pytest.mark.parametrize("args,rc", [
+    ((FAKE, FAKE, 0, 64, 128, FAKE), INVALID), ((FAKE, FAKE, 129, 64, 128, FAKE), UNSUPPORTED),
+    ((FAKE, FAKE, 4, 60, 128, FAKE), UNSUPPORTED), ((None, FAKE, 4, 64, 128, FAKE), INVALID),
+    ((FAKE, FAKE, 4, 64, 128, FAKE + 8), INVALID),
+])
+def test_ffn_pack_rejects(lib, args, rc):
+    assert lib.mova_ffn_pack_gate_up(*args, None) == rc
 
 
 def test_dense_workspace_bytes(lib):

@@ -1,0 +1,118 @@
+"""FFN mixture of experts (mova_ffn_moe_forward) vs the CPU oracle.
+
+Routing: the index / weight rules of ``paritylib.check_routing`` on every
+token.  Outputs: the output rules on every token (sampled rows at T = 4096),
+against the oracle evaluated with the GPU's choice on near-tie tokens.  Also:
+the gate/up interleaving, a token's row not depending on the other tokens,
+and no shared expert.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_value_projection_amd import binding, inputs
+import paritylib as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    binding.load_library()
+    yield
+
+
+def gpu_layer(sh, seed):
+    L = inputs.make_ffn_layer(sh, seed)
+    g = {k: v.to(DEV).contiguous() for k, v in L.items()}
+    g["gate_up_w"] = binding.ffn_pack_gate_up(g["gate_w"], g["up_w"])
+    if sh.inter_shared:
+        g["shared_gate_up_w"] = binding.ffn_pack_gate_up(g["shared_gate_w"], g["shared_up_w"])
+    return L, g
+
+
+def run_ffn(g, sh, x=None):
+    x = g["x"] if x is None else x
+    T = x.shape[0]
+    idx = torch.empty(T, sh.k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, sh.k, dtype=torch.float32, device=DEV)
+    out = binding.ffn_moe_forward(x, g["router_w"], g["router_b"], g["gate_up_w"], g["down_w"],
+                                  sh.k, sh.scale, g.get("shared_gate_up_w"),
+                                  g.get("shared_down_w"), topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    return out, idx, w
+
+
+def ffn_reference(L, sh, rows, eff_idx, eff_w):
+    """The oracle's experts on the given rows with the routing to check."""
+    o = {k: v.double().numpy() for k, v in L.items()}
+    x = o["x"][rows]
+    out = np.zeros((len(rows), sh.d))
+    for n, t in enumerate(rows):
+        for j in range(sh.k):
+            e = int(eff_idx[t, j])
+            out[n] += eff_w[t, j] * oracle.swiglu_expert(x[n:n + 1], o["gate_w"][e], o["up_w"][e],
+                                                         o["down_w"][e])[0]
+    if sh.inter_shared:
+        out += oracle.swiglu_expert(x, o["shared_gate_w"], o["shared_up_w"], o["shared_down_w"])
+    return out
+
+
+CASES = [
+    # T, d, E, k, inter, inter_shared
+    (37, 256, 12, 3, 64, 64),
+    (64, 2560, 100, 8, 768, 768),
+    (300, 512, 100, 8, 128, 0),
+    (200, 192, 8, 8, 64, 128),
+    (4096, 2560, 100, 8, 768, 768),
+]
+
+
+@pytest.mark.parametrize("T,d,E,k,inter,inter_s", CASES)
+def test_ffn_matches_oracle(T, d, E, k, inter, inter_s):
+    sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s)
+    say(f"ffn T={T} d={d} E={E} k={k} inter={inter} shared={inter_s}")
+    L, g = gpu_layer(sh, seed=T + E)
+    out, idx, w = run_ffn(g, sh)
+    o = {kk: v.double().numpy() for kk, v in L.items()}
+    ref = oracle.route(o["x"], o["router_w"], o["router_b"], k, sh.scale)
+    rc = P.check_routing(idx, w, ref, sh.scale)
+    rows = np.arange(T) if T <= 512 else np.unique(
+        np.r_[np.random.default_rng(3).choice(T, 200, replace=False), 0, T - 1])
+    want = ffn_reference(L, sh, rows, rc.effective_idx, rc.effective_w)
+    got = out[torch.as_tensor(rows, device=DEV)]
+    st = P.check_output(got, want, what=f"ffn T={T}")
+    say(f"  {st} near_ties={rc.near_ties}")
+
+
+def test_ffn_pack_gate_up_layout():
+    E, inter, d = 3, 64, 128
+    gate = torch.randn(E, inter, d, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    up = torch.randn(E, inter, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    got = binding.ffn_pack_gate_up(gate.to(DEV), up.to(DEV)).cpu()
+    want = torch.empty(E, 2 * inter, d, dtype=torch.bfloat16)
+    for b in range(inter // 16):
+        want[:, 32 * b:32 * b + 16] = gate[:, 16 * b:16 * b + 16]
+        want[:, 32 * b + 16:32 * b + 32] = up[:, 16 * b:16 * b + 16]
+    assert torch.equal(got, want)
+
+
+def test_ffn_rows_do_not_depend_on_other_tokens():
+    sh = inputs.FfnShape(T=600, d=512, E=100, k=8, inter=128, inter_shared=64)
+    L, g = gpu_layer(sh, seed=9)
+    full, idx, w = run_ffn(g, sh)
+    part, idx2, w2 = run_ffn(g, sh, g["x"][123:323].contiguous())
+    assert torch.equal(idx[123:323], idx2) and torch.equal(w[123:323], w2)
+    assert torch.equal(full[123:323], part)
+    again, _, _ = run_ffn(g, sh)
+    assert torch.equal(full, again)

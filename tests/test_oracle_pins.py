@@ -360,6 +360,68 @@ def test_rebuild_repeated_and_negative_ids():
     assert (oracle.rebuild_values(x, W, [[-1, 4]] * 3, [[1.0, 1.0]] * 3) == 0).all()
 
 
+# ------------------------------------------------ FFN mixture of experts
+
+def test_swiglu_hand_example():
+    """Worked by hand: gate picks x0 = 1, up picks x1 = 2, so h = SiLU(1) * 2
+    = 2 / (1 + exp(-1)); down maps h to (3h, -h)."""
+    x = np.array([[1.0, 2.0]])
+    h = 2.0 / (1.0 + math.exp(-1.0))
+    got = oracle.swiglu_expert(x, [[1.0, 0.0]], [[0.0, 1.0]], [[3.0], [-1.0]])
+    np.testing.assert_allclose(got, [[3 * h, -h]], rtol=1e-15, atol=0)
+
+
+def ffn_brute_force(x, wr, b, G, U, D, k, scale, shared):
+    """Every expert on every token (einsum), masked to a top-k chosen by a
+    plain Python sort; independent of the oracle's code."""
+    logits = np.einsum("td,ed->te", x, wr)
+    s = 1.0 / (1.0 + np.exp(-logits))
+    g = np.einsum("td,eid->tei", x, G)
+    u = np.einsum("td,eid->tei", x, U)
+    y_all = np.einsum("tei,eoi->teo", g / (1.0 + np.exp(-g)) * u, D)
+    out = np.zeros((x.shape[0], D.shape[1]))
+    for t in range(x.shape[0]):
+        chosen = sorted(range(len(b)), key=lambda e: (-(s[t, e] + b[e]), e))[:k]
+        den = sum(s[t, e] for e in chosen)
+        for e in chosen:
+            out[t] += scale * s[t, e] / den * y_all[t, e]
+    sg, su, sd = shared
+    hs = x @ sg.T
+    out += (hs / (1.0 + np.exp(-hs)) * (x @ su.T)) @ sd.T
+    return out
+
+
+def test_ffn_moe_brute_force():
+    rng = np.random.default_rng(40)
+    T, d, E, k, I = 7, 24, 12, 3, 8
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d)) * 0.3
+    b = rng.uniform(-0.01, 0.01, E)
+    G, U = rng.standard_normal((2, E, I, d)) / 5
+    D = rng.standard_normal((E, d, I)) / 3
+    shared = (rng.standard_normal((I, d)) / 5, rng.standard_normal((I, d)) / 5,
+              rng.standard_normal((d, I)) / 3)
+    got, r = oracle.ffn_moe_forward(x, wr, b, G, U, D, k, 2.5, shared)
+    np.testing.assert_allclose(got, ffn_brute_force(x, wr, b, G, U, D, k, 2.5, shared),
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r.w.sum(axis=1), 2.5, rtol=1e-14)
+
+
+def test_ffn_moe_identical_experts_reduce_to_one_scaled_expert():
+    """With every routed expert identical, the mixture is scale times that
+    expert (the weights sum to the scale), plus the shared expert."""
+    rng = np.random.default_rng(41)
+    T, d, E, k, I = 5, 16, 6, 2, 8
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    g1, u1 = rng.standard_normal((2, I, d)) / 4
+    d1 = rng.standard_normal((d, I)) / 3
+    G, U, D = np.tile(g1, (E, 1, 1)), np.tile(u1, (E, 1, 1)), np.tile(d1, (E, 1, 1))
+    got, _ = oracle.ffn_moe_forward(x, wr, np.zeros(E), G, U, D, k, 1.75, None)
+    np.testing.assert_allclose(got, 1.75 * oracle.swiglu_expert(x, g1, u1, d1), rtol=1e-12,
+                               atol=1e-13)
+
+
 def test_skewed_workload_load_ratio():
     """The skewed workload's bias gives max / mean expert load of 10 (+-5%)."""
     w = inputs.WORKLOADS["skewed"]
