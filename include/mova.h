@@ -237,7 +237,8 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
  * bf16 (the down projection's MFMA operand); each routed slot's w * down(h)
  * and the shared expert's output are kept as fp16; the sum is fp32 in slot
  * order, the shared term last, rounded once to bf16.  Logits for the top-k
- * are one fp32 MFMA chain per (token, expert) over d in order.  Errors as for
+ * are fp32: four MFMA chains per (token, expert) over the k steps of each
+ * residue class mod 4, in order, added in class order.  Errors as for
  * mova_value_forward.
  */
 size_t mova_ffn_workspace_bytes(int T, int d, int E, int k, int inter, int inter_shared);

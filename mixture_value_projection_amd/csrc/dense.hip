@@ -126,31 +126,67 @@ __global__ __launch_bounds__(256) void dense_skinny_kernel(const bf16_t* __restr
   }
 }
 
-// out[t, n] = bf16( sum_{s < S} part[s, t, n] ), s in order; 8 columns per thread.
+// out[t, n] = bf16( sum_{s < S} part[s, t, n] ), s in order; 8 columns per
+// thread.  kOut selects the output: kDenseOutBf16 as above; kDenseOutF16 the
+// same sum rounded to fp16; kDenseOutSwiGLU the SwiGLU of gate / up columns
+// interleaved in blocks of 16 (column 32b + j is gate 16b + j, column
+// 32b + 16 + j the matching up), out[t, c] = bf16(SiLU(gate_c) * up_c) with
+// N / 2 columns.
+__device__ __forceinline__ void split_sum8(const float* __restrict__ part, size_t plane, int S,
+                                           size_t o, float (&v)[8]) {
+  f32x4 lo = *reinterpret_cast<const f32x4*>(part + o);
+  f32x4 hi = *reinterpret_cast<const f32x4*>(part + o + 4);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 l2 = *reinterpret_cast<const f32x4*>(part + s * plane + o);
+    const f32x4 h2 = *reinterpret_cast<const f32x4*>(part + s * plane + o + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo[j] += l2[j];
+      hi[j] += h2[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = lo[j];
+    v[j + 4] = hi[j];
+  }
+}
+
+template <int kOut>
 __global__ __launch_bounds__(256) void dense_split_reduce_kernel(const float* __restrict__ part,
-                                                                 bf16_t* __restrict__ out, int T,
+                                                                 void* __restrict__ out, int T,
                                                                  int N, int S) {
-  const long long total = (long long)T * N / 8;
+  const int NO = kOut == kDenseOutSwiGLU ? N / 2 : N;  // output columns
+  const long long total = (long long)T * NO / 8;
   const size_t plane = (size_t)T * N;
   for (long long v = blockIdx.x * 256ll + threadIdx.x; v < total; v += (long long)gridDim.x * 256) {
-    const size_t o = (size_t)v * 8;
-    f32x4 lo = *reinterpret_cast<const f32x4*>(part + o);
-    f32x4 hi = *reinterpret_cast<const f32x4*>(part + o + 4);
-    for (int s = 1; s < S; ++s) {
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(part + s * plane + o);
-      const f32x4 h2 = *reinterpret_cast<const f32x4*>(part + s * plane + o + 4);
+    const size_t oo = (size_t)v * 8;  // first output element
+    float r[8];
+    if constexpr (kOut == kDenseOutSwiGLU) {
+      const size_t t = oo / NO;
+      const int c = (int)(oo % NO);
+      const size_t gcol = (size_t)(c / 16) * 32 + (c % 16);
+      float g[8], u[8];
+      split_sum8(part, plane, S, t * N + gcol, g);
+      split_sum8(part, plane, S, t * N + gcol + 16, u);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo[j] += l2[j];
-        hi[j] += h2[j];
-      }
+      for (int j = 0; j < 8; ++j) r[j] = siluf(g[j]) * u[j];
+    } else {
+      split_sum8(part, plane, S, oo, r);
     }
     u32x4 packed;
-    packed[0] = (uint32_t)f32_to_bf16_bits(lo[0]) | ((uint32_t)f32_to_bf16_bits(lo[1]) << 16);
-    packed[1] = (uint32_t)f32_to_bf16_bits(lo[2]) | ((uint32_t)f32_to_bf16_bits(lo[3]) << 16);
-    packed[2] = (uint32_t)f32_to_bf16_bits(hi[0]) | ((uint32_t)f32_to_bf16_bits(hi[1]) << 16);
-    packed[3] = (uint32_t)f32_to_bf16_bits(hi[2]) | ((uint32_t)f32_to_bf16_bits(hi[3]) << 16);
-    store16(out + o, packed);
+    if constexpr (kOut == kDenseOutF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        packed[i] = (uint32_t)__builtin_bit_cast(uint16_t, (f16_t)r[2 * i]) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (f16_t)r[2 * i + 1]) << 16);
+      store16((f16_t*)out + oo, packed);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        packed[i] = (uint32_t)f32_to_bf16_bits(r[2 * i]) | ((uint32_t)f32_to_bf16_bits(r[2 * i + 1]) << 16);
+      store16((bf16_t*)out + oo, packed);
+    }
   }
 }
 
@@ -174,9 +210,16 @@ hipError_t launch_dense_skinny(const DenseArgs& a, hipStream_t stream) {
   kern<<<grid, 256, lds, stream>>>(a.x, a.W, a.part, a.T, a.d, a.N);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const long long total = (long long)a.T * a.N / 8;
+  const int NO = a.out_mode == kDenseOutSwiGLU ? a.N / 2 : a.N;
+  const long long total = (long long)a.T * NO / 8;
   const long long blocks = std::min<long long>((total + 255) / 256, 256ll * 16);
-  dense_split_reduce_kernel<<<dim3((unsigned)blocks), 256, 0, stream>>>(a.part, a.out, a.T, a.N, S);
+  const dim3 g((unsigned)blocks);
+  if (a.out_mode == kDenseOutSwiGLU)
+    dense_split_reduce_kernel<kDenseOutSwiGLU><<<g, 256, 0, stream>>>(a.part, a.out_any, a.T, a.N, S);
+  else if (a.out_mode == kDenseOutF16)
+    dense_split_reduce_kernel<kDenseOutF16><<<g, 256, 0, stream>>>(a.part, a.out_any, a.T, a.N, S);
+  else
+    dense_split_reduce_kernel<kDenseOutBf16><<<g, 256, 0, stream>>>(a.part, a.out, a.T, a.N, S);
   return hipGetLastError();
 }
 

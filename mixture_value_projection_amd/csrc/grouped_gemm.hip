@@ -31,7 +31,7 @@
 //
 // Tile choice (measured on the decode, prefill, chunked and skewed shapes):
 // grouped mode takes 128 x 128 (2 stages, two workgroups per CU) while the
-// experts average at most 256 rows, else 256 x 256; dense mode takes 256 x
+// experts average at most 384 rows, else 256 x 256; dense mode takes 256 x
 // 256 once those tiles fill the 256 CUs, else 128 x 128 with 4 stages when
 // the grid is a single round of workgroups and 2 stages otherwise.
 //
@@ -108,8 +108,9 @@ GemmTile gemm_tile_grouped(int T, int k, int E) {
   GemmTile t;
   if (forced_tile(&t)) return t;
   // 128 x 128 tiles (two workgroups per CU) while the experts average at most
-  // 256 rows, where 256-row tiles are mostly padding; 256 x 256 above.
-  if ((long long)T * k <= 256ll * E) return {128, 128, 8, 2};
+  // 384 rows (one and a half 256-row tiles), where 256-row tiles carry much
+  // padding; 256 x 256 above.
+  if ((long long)T * k <= 384ll * E) return {128, 128, 8, 2};
   return {256, 256, 8, 2};
 }
 

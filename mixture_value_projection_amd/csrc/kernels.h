@@ -88,12 +88,22 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 GemmTile gemm_tile_dense(int T, int N);
 hipError_t launch_dense_gemm(const GemmArgs& a, hipStream_t stream);
 
+// Output of the split-k dense kernel's reduction.
+enum DenseOut {
+  kDenseOutBf16 = 0,   // out bf16 [T, N]
+  kDenseOutF16 = 1,    // out_any fp16 [T, N]
+  kDenseOutSwiGLU = 2  // out_any bf16 [T, N / 2]: SiLU(gate) * up of gate / up rows
+                       // interleaved in blocks of 16 (as the SwiGLU GEMM modes)
+};
+
 struct DenseArgs {
   const __bf16* x;  // [T, d]
   const __bf16* W;  // [N, d]
   float* part;      // [dense_skinny_splits(d), T, N] fp32 scratch
-  __bf16* out;      // [T, N]
+  __bf16* out;      // [T, N] (kDenseOutBf16)
   int T, d, N;
+  int out_mode = kDenseOutBf16;
+  void* out_any = nullptr;  // kDenseOutF16 / kDenseOutSwiGLU output
 };
 // The split-k dense kernel handles at most this many tokens per call.
 constexpr int kDenseSkinnyMaxT = 256;
@@ -132,11 +142,13 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
-// FFN mixture of experts (ffn.hip): router for E <= kMaxDispatchExperts (one
-// workgroup per ffn_router_chunk_tokens() tokens, which is also the dispatch
+// FFN mixture of experts (ffn.hip): router for E <= kMaxDispatchExperts
+// (partial logits in plog, ffn_router_plog_floats(T) floats; selection in
+// workgroups of ffn_router_chunk_tokens() tokens, which is also the dispatch
 // chunk; chunk_counts [blocks, E]), and the gate/up row interleaving.
 int ffn_router_chunk_tokens();
-hipError_t launch_ffn_router(const RouterArgs& a, hipStream_t stream);
+int ffn_router_plog_floats(int T);
+hipError_t launch_ffn_router(const RouterArgs& a, float* plog, hipStream_t stream);
 hipError_t launch_ffn_pack_gate_up(const __bf16* gate, const __bf16* up, __bf16* dst, int E,
                                    int inter, int d, hipStream_t stream);
 

@@ -125,11 +125,13 @@ int check_ffn(int T, int d, int E, int k, int inter, int inter_shared) {
 
 // FFN workspace (every region 256-byte aligned):
 //   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] |
-//   tile_base [E+1] | perm [T*k] i32 | h [T*k, inter] bf16 | partial [T*k, d] f16 |
-//   shared h [T, inter_shared] bf16 | shared partial [T, d] f16
+//   tile_base [E+1] | router partial logits | perm [T*k] i32 |
+//   h [T*k, inter] bf16 | partial [T*k, d] f16 |
+//   shared h [T, inter_shared] bf16 | shared partial [T, d] f16 |
+//   split-k fp32 partials of the shared expert (T <= kDenseSkinnyMaxT only)
 // C = ceil(T / ffn_router_chunk_tokens()).
 struct FfnLayout {
-  size_t idx, w, chunk, eoff, tbase, perm, h, partial, hs, ps, total;
+  size_t idx, w, chunk, eoff, tbase, plog, perm, h, partial, hs, ps, sk, total;
 };
 
 FfnLayout ffn_layout(int T, int d, int E, int k, int inter, int inter_shared) {
@@ -142,11 +144,16 @@ FfnLayout ffn_layout(int T, int d, int E, int k, int inter, int inter_shared) {
   L.chunk = o;   o += align256(C * E * 4);
   L.eoff = o;    o += align256((size_t)(E + 1) * 4);
   L.tbase = o;   o += align256((size_t)(E + 1) * 4);
+  L.plog = o;    o += align256((size_t)ffn_router_plog_floats(T) * 4);
   L.perm = o;    o += align256(pairs * 4);
   L.h = o;       o += align256(pairs * inter * 2);
   L.partial = o; o += align256(pairs * d * 2);
   L.hs = o;      o += align256((size_t)T * inter_shared * 2);
   L.ps = o;      o += align256(inter_shared > 0 ? (size_t)T * d * 2 : 0);
+  L.sk = o;
+  if (inter_shared > 0 && T <= kDenseSkinnyMaxT)
+    o += align256(std::max(dense_skinny_partial_floats(T, d, 2 * inter_shared),
+                           dense_skinny_partial_floats(T, inter_shared, d)) * 4);
   L.total = o;
   return L;
 }
@@ -458,7 +465,7 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
   {
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w, chunk};
-    err = launch_ffn_router(ra, stream);
+    err = launch_ffn_router(ra, (float*)(ws + L.plog), stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
   const GemmTile tile = gemm_tile_grouped(T, k, E);
@@ -480,7 +487,19 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
                   T, inter, d, E, k, tile, kGemmRoutedLinear};
       err = launch_grouped_gemm(dn, stream);
     }
-    if (err == hipSuccess && inter_shared > 0) {
+    if (err == hipSuccess && inter_shared > 0 && T <= kDenseSkinnyMaxT) {
+      // Few tokens: the weight-streaming split-k kernel, whose reduction
+      // applies the SwiGLU (gate/up) or rounds to fp16 (down).
+      float* sk = (float*)(ws + L.sk);
+      DenseArgs sg{xb, (const __bf16*)shared_gate_up_w, sk, nullptr, T, d, 2 * inter_shared,
+                   kDenseOutSwiGLU, hs};
+      err = launch_dense_skinny(sg, stream);
+      if (err == hipSuccess) {
+        DenseArgs sd{hs, (const __bf16*)shared_down_w, sk, nullptr, T, inter_shared, d,
+                     kDenseOutF16, ps};
+        err = launch_dense_skinny(sd, stream);
+      }
+    } else if (err == hipSuccess && inter_shared > 0) {
       GemmArgs sg{xb, (const __bf16*)shared_gate_up_w, nullptr, nullptr, nullptr, nullptr,
                   nullptr, hs, T, d, 2 * inter_shared, 1, 1, {0, 0, 0, 0}, kGemmDenseSwiGLU};
       err = launch_dense_gemm(sg, stream);

@@ -74,6 +74,8 @@ CASES = [
     (64, 2560, 100, 8, 768, 768),
     (300, 512, 100, 8, 128, 0),
     (200, 192, 8, 8, 64, 128),
+    (256, 256, 100, 8, 64, 192),
+    (257, 256, 100, 8, 64, 192),
     (4096, 2560, 100, 8, 768, 768),
 ]
 
