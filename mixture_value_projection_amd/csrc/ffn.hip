@@ -45,7 +45,6 @@ __device__ __forceinline__ uint32_t order_key(float sel) {
 // Weights: scale * s_j / (sum of the k chosen sigmoid scores, added in rank
 // order).  The workgroup's per-expert pair counts go to counts[blockIdx.x, :]
 // for the dispatch.
-constexpr int kFfnTiles = kMaxDispatchExperts / 16;  // expert column tiles
 
 int ffn_router_plog_floats(int T) { return 4 * ceil_div(T, kFfnTokens) * kFfnTokens * kMaxDispatchExperts; }
 
