@@ -31,14 +31,14 @@ __device__ __forceinline__ uint32_t order_key(float sel) {
 // Router in two kernels, so that even a few tokens spread the router weight
 // over many CUs.
 //
-// ffn_logits_kernel: one wave per (16 tokens, 16 experts, quarter of d);
-// quarter c runs k steps c, c + 4, c + 8, ... as one MFMA chain in increasing
-// order (token fragments and router rows read straight from cache) and
-// writes plog[c][t][e].
+// ffn_logits_kernel: one wave per (16 tokens, 16 experts, residue class c of
+// the 32-wide k steps mod 4); class c runs steps c, c + 4, c + 8, ... as one
+// MFMA chain in increasing order (token fragments and router rows read
+// straight from cache) and writes plog[c][t][e].
 //
 // ffn_topk_kernel: one workgroup per 16 tokens (the dispatch chunk), one
-// wave per token.  Logits are the quarters added in order, ((q0 + q1) + q2)
-// + q3.  Lane l holds experts l and l + 64; each of the k rounds takes the
+// wave per token.  Logits are the four class sums added in class order,
+// ((c0 + c1) + c2) + c3.  Lane l holds experts l and l + 64; each of the k rounds takes the
 // wave-wide maximum of a 64-bit key (selection score's bits mapped to an
 // order-keeping unsigned integer, then 127 - expert, so equal scores rank
 // the lower expert first) and drops the winner.
@@ -46,7 +46,9 @@ __device__ __forceinline__ uint32_t order_key(float sel) {
 // order).  The workgroup's per-expert pair counts go to counts[blockIdx.x, :]
 // for the dispatch.
 
-int ffn_router_plog_floats(int T) { return 4 * ceil_div(T, kFfnTokens) * kFfnTokens * kMaxDispatchExperts; }
+size_t ffn_router_plog_floats(int T) {
+  return (size_t)4 * ceil_div(T, kFfnTokens) * kFfnTokens * kMaxDispatchExperts;
+}
 
 __global__ __launch_bounds__(64) void ffn_logits_kernel(const bf16_t* __restrict__ x,
                                                         const bf16_t* __restrict__ wr, int T, int d,
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kTopkThreads) void ffn_topk_kernel(const float* __r
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int tw = blockIdx.x * kFfnTokens + wave * NT;  // the wave's first token
-  const size_t cs = (size_t)gridDim.x * kFfnTokens * kMaxDispatchExperts;  // one quarter
+  const size_t cs = (size_t)gridDim.x * kFfnTokens * kMaxDispatchExperts;  // one class plane
   if (tid < kMaxDispatchExperts) hist[tid] = 0;
   __syncthreads();
   const float b0 = (bias != nullptr && lane < E) ? bias[lane] : 0.f;

@@ -147,7 +147,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 // workgroups of ffn_router_chunk_tokens() tokens, which is also the dispatch
 // chunk; chunk_counts [blocks, E]), and the gate/up row interleaving.
 int ffn_router_chunk_tokens();
-int ffn_router_plog_floats(int T);
+size_t ffn_router_plog_floats(int T);
 hipError_t launch_ffn_router(const RouterArgs& a, float* plog, hipStream_t stream);
 hipError_t launch_ffn_pack_gate_up(const __bf16* gate, const __bf16* up, __bf16* dst, int E,
                                    int inter, int d, hipStream_t stream);

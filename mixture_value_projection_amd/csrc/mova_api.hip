@@ -144,7 +144,7 @@ FfnLayout ffn_layout(int T, int d, int E, int k, int inter, int inter_shared) {
   L.chunk = o;   o += align256(C * E * 4);
   L.eoff = o;    o += align256((size_t)(E + 1) * 4);
   L.tbase = o;   o += align256((size_t)(E + 1) * 4);
-  L.plog = o;    o += align256((size_t)ffn_router_plog_floats(T) * 4);
+  L.plog = o;    o += align256(ffn_router_plog_floats(T) * 4);
   L.perm = o;    o += align256(pairs * 4);
   L.h = o;       o += align256(pairs * inter * 2);
   L.partial = o; o += align256(pairs * d * 2);
