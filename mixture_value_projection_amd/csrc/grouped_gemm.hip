@@ -48,6 +48,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -310,25 +312,35 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     // Ring of kS stages, loads kS - 1 steps ahead.  Step kt: wait for this
     // wave's loads of step kt (the kS - 2 later steps may stay in flight) and
     // for its LDS reads, barrier (every wave's loads of step kt have landed,
-    // and every wave is done reading step kt - 1's stage), refill that stage
-    // with step kt + kS - 1, then run step kt's MFMAs.  Steps past KT load
+    // and every wave is done reading step kt - 1's stage), run step kt's
+    // MFMAs, then refill step kt - 1's stage with step kt + kS - 1.  (Issued
+    // after the fragment reads, the refill keeps the compiler from waiting on
+    // every outstanding direct load before those reads.)  Steps past KT load
     // step KT - 1 again (never read), so every step issues the same number of
-    // loads and the wait count stays exact.
+    // loads and the wait count stays exact.  Waves without valid rows run the
+    // same loop without the MFMAs.
     constexpr int L = TL::kLoadsA + TL::kLoadsB;
     __syncthreads();  // the tile's pair / weight table is written
 #pragma unroll
     for (int st = 0; st < kS - 1; ++st)
       issue_loads<MOVA_TILE_ARGS>(c, smem + st * TL::kStage, wave, min(st, KT - 1) * kRowBytes);
-    for (int kt = 0; kt < KT; ++kt) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kS - 2) * L));
-      raw_barrier();
-      const int nk = kt + kS - 1;
-      issue_loads<MOVA_TILE_ARGS>(c, smem + (nk % kS) * TL::kStage, wave,
-                                  min(nk, KT - 1) * kRowBytes);
-      if (active) mma_step<MOVA_TILE_ARGS>(acc, smem + (kt % kS) * TL::kStage, wm, wn, q, r16);
+    auto ring = [&](auto compute) {
+      for (int kt = 0; kt < KT; ++kt) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kS - 2) * L));
+        raw_barrier();
+        const int nk = kt + kS - 1;
+        if constexpr (decltype(compute)::value)
+          mma_step<MOVA_TILE_ARGS>(acc, smem + (kt % kS) * TL::kStage, wm, wn, q, r16);
+        issue_loads<MOVA_TILE_ARGS>(c, smem + (nk % kS) * TL::kStage, wave,
+                                    min(nk, KT - 1) * kRowBytes);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+    };
+    if (!active) {
+      ring(std::false_type{});
+      return;
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    if (!active) return;
+    ring(std::true_type{});
   }
 
   // Epilogue (see the mode table above).
