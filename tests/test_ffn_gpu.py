@@ -75,14 +75,20 @@ CASES = [
     (300, 512, 100, 8, 128, 0),
     (200, 192, 8, 8, 64, 128),
     (256, 256, 100, 8, 64, 192),
+    (100, 128, 128, 8, 64, 0),     # E at its maximum: every lane holds two experts
+    (20, 64, 1, 1, 64, 64, 1.0),   # one expert, k = 1 (scale 1: the whole scale lands on
+                                   # one expert, and 2.5 would push |out| past the range
+                                   # the max-abs rule is set for)
     (257, 256, 100, 8, 64, 192),
     (4096, 2560, 100, 8, 768, 768),
 ]
 
 
-@pytest.mark.parametrize("T,d,E,k,inter,inter_s", CASES)
-def test_ffn_matches_oracle(T, d, E, k, inter, inter_s):
-    sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s)
+@pytest.mark.parametrize("case", CASES)
+def test_ffn_matches_oracle(case):
+    T, d, E, k, inter, inter_s = case[:6]
+    scale = case[6] if len(case) > 6 else 2.5
+    sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s, scale=scale)
     say(f"ffn T={T} d={d} E={E} k={k} inter={inter} shared={inter_s}")
     L, g = gpu_layer(sh, seed=T + E)
     out, idx, w = run_ffn(g, sh)
