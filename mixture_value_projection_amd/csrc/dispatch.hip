@@ -24,51 +24,75 @@
 namespace mova {
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanCols = kMaxDispatchExperts;              // one thread per expert
-constexpr int kScanGroups = kScanThreads / kScanCols;       // chunk ranges
+constexpr int kScanMaxGroups = kScanThreads / 64;  // chunk ranges at E <= 64
+constexpr int kScanRegs = 32;  // counts a thread keeps in registers between passes
 
-// One workgroup; thread column = expert, so every count load is a contiguous
-// row of the [C, E] table.  Group w owns chunks [w * per, (w + 1) * per).
+// One workgroup.  Thread column = expert (64 columns when E <= 64, else 128),
+// so every count load is a contiguous row of the [C, E] table; the
+// 1024 / columns groups split the chunks, group w owning chunks
+// [w * per, (w + 1) * per).  Pass 1 sums each thread's counts, the groups'
+// sums give each range its starting offset, pass 2 rewrites the counts as
+// offsets.  With at most kScanRegs chunks per thread (C <= 512 at E <= 64)
+// the counts stay in registers between the passes, so the table is read
+// once.
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     int32_t* __restrict__ counts, int C, int E, int block_m,
     int32_t* __restrict__ expert_off, int32_t* __restrict__ tile_base) {
-  __shared__ int wave_sum[kScanGroups][kScanCols];
-  __shared__ int total[kScanCols];
-  __shared__ int mtiles[kScanCols];
-  const int e = threadIdx.x % kScanCols;
-  const int w = threadIdx.x / kScanCols;
-  const int per = ceil_div(C, kScanGroups);
+  __shared__ int wave_sum[kScanMaxGroups][kMaxDispatchExperts];
+  __shared__ int total[kMaxDispatchExperts];
+  __shared__ int mtiles[kMaxDispatchExperts];
+  const int cols = E <= 64 ? 64 : kMaxDispatchExperts;
+  const int groups = kScanThreads / cols;
+  const int e = threadIdx.x % cols;
+  const int w = threadIdx.x / cols;
+  const int per = ceil_div(C, groups);
   const int c0 = min(C, w * per), c1 = min(C, c0 + per);
   const bool live = e < E;
+  const bool cached = per <= kScanRegs;  // uniform
 
   int s = 0;
-  if (live) {
+  int v[kScanRegs];
+  if (cached) {
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) v[i] = (live && c0 + i < c1) ? counts[(size_t)(c0 + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanRegs; ++i) s += v[i];
+  } else if (live) {
     for (int cb = c0; cb < c1; cb += 16) {
-      int v[16];
+      int u[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
+      for (int i = 0; i < 16; ++i) u[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s += v[i];
+      for (int i = 0; i < 16; ++i) s += u[i];
     }
   }
   wave_sum[w][e] = s;
   __syncthreads();
   int run = 0;
   for (int i = 0; i < w; ++i) run += wave_sum[i][e];
-  if (w == kScanGroups - 1) {
+  if (w == groups - 1) {
     total[e] = live ? run + s : 0;
     mtiles[e] = live ? ceil_div(run + s, block_m) : 0;
   }
-  // Rewrite counts as offsets; each block of 16 is loaded before any store.
-  if (live) {
-    for (int cb = c0; cb < c1; cb += 16) {
-      int v[16];
+  // Rewrite counts as offsets (reloading, block by block, when they were not
+  // kept: each block of 16 is loaded before any of its stores).
+  if (cached) {
+    if (live) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
+      for (int i = 0; i < kScanRegs; ++i) {
+        if (c0 + i < c1) counts[(size_t)(c0 + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+  } else if (live) {
+    for (int cb = c0; cb < c1; cb += 16) {
+      int u[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = (cb + i < c1) ? counts[(size_t)(cb + i) * E + e] : 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (cb + i < c1) counts[(size_t)(cb + i) * E + e] = run;
-        run += v[i];
+        run += u[i];
       }
     }
   }
@@ -78,7 +102,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     // (entries past E are zero).
     int off = 0, tiles = 0, all = 0, all_tiles = 0;
 #pragma unroll 16
-    for (int i = 0; i < kScanCols; ++i) {
+    for (int i = 0; i < cols; ++i) {
       const int t = total[i];
       const int mt = mtiles[i];
       off += i < e ? t : 0;
