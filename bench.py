@@ -112,6 +112,7 @@ def run_single_layer(name, steps, warmup, copies):
     torch.cuda.synchronize()
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=sh.E)
     touched = int((counts > 0).sum())
+    max_abs_out = float(out.float().abs().max())  # the parity budget assumes |out| < 8
 
     def mk(c):
         return lambda: binding.value_forward(x, c["router_w"], c["router_b"], c["expert_w"], sh.k,
@@ -123,7 +124,8 @@ def run_single_layer(name, steps, warmup, copies):
     tokens = sh.T * steps
     return dict(shape=sh, seconds=secs, tokens=tokens, calls=steps, stage_ms=stage_ms,
                 stage_records=nrec, graph_seconds=gsecs, graph_calls=gcalls,
-                touched=touched, max_load=int(counts.max()), mean_load=float(counts.mean()))
+                touched=touched, max_load=int(counts.max()), mean_load=float(counts.mean()),
+                max_abs_out=max_abs_out)
 
 
 def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
@@ -308,6 +310,7 @@ def prefill_line(name, r):
         "tokens_per_s": gtokens / r["graph_seconds"],
         "ms_per_call": 1e3 * r["graph_seconds"] / r["graph_calls"],
         "eager_tokens_per_s": r["tokens"] / r["seconds"],
+        "max_abs_out": r["max_abs_out"],
         "tflops": tflops,
         "frac_bf16_peak": tflops * 1e12 / accounting.BF16_MFMA_PEAK_FLOPS,
         "grouped_gemm_us": 1e3 * r["stage_ms"],
@@ -454,6 +457,7 @@ def main():
                                   args.copies if name == "prefill" else 2)
             d = prefill_line(name, rr)
             d["max_over_mean_load"] = rr["max_load"] / rr["mean_load"]
+            d["max_abs_out"] = rr["max_abs_out"]
             sec.append(d)
             torch.cuda.empty_cache()
         log("chunked workload ...")
