@@ -310,7 +310,6 @@ def prefill_line(name, r):
         "tokens_per_s": gtokens / r["graph_seconds"],
         "ms_per_call": 1e3 * r["graph_seconds"] / r["graph_calls"],
         "eager_tokens_per_s": r["tokens"] / r["seconds"],
-        "max_abs_out": r["max_abs_out"],
         "tflops": tflops,
         "frac_bf16_peak": tflops * 1e12 / accounting.BF16_MFMA_PEAK_FLOPS,
         "grouped_gemm_us": 1e3 * r["stage_ms"],
@@ -437,6 +436,7 @@ def main():
         "timing": "steps replayed from a HIP graph of rotated-copy calls; eager "
                   "per-call launches give eager_tokens_per_s",
         "eager_tokens_per_s": r["tokens"] / r["seconds"],
+        "max_abs_out": r["max_abs_out"],
         "whole_call": {"GB_per_s": call_bytes / step_s / 1e9,
                        "frac_hbm": call_bytes / step_s / accounting.HBM_PEAK_BPS,
                        "bytes": call_bytes},

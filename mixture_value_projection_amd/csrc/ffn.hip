@@ -31,8 +31,8 @@ __device__ __forceinline__ uint32_t order_key(float sel) {
 // Router in two kernels, so that even a few tokens spread the router weight
 // over many CUs.
 //
-// ffn_logits_kernel: one wave per (16 tokens, 16 experts, residue class c of
-// the 32-wide k steps mod 4); class c runs steps c, c + 4, c + 8, ... as one
+// ffn_logits_kernel: one wave per (16 tokens, 16 or 64 experts, residue
+// class c of the 32-wide k steps mod 4); class c runs steps c, c + 4, c + 8, ... as one
 // MFMA chain in increasing order (token fragments and router rows read
 // straight from cache) and writes plog[c][t][e].
 //
@@ -50,37 +50,52 @@ size_t ffn_router_plog_floats(int T) {
   return (size_t)4 * ceil_div(T, kFfnTokens) * kFfnTokens * kMaxDispatchExperts;
 }
 
+// TPW: expert tiles per wave (sharing the token fragments); 1 for few
+// tokens, where the number of waves matters more than the loads they share.
+template <int TPW>
 __global__ __launch_bounds__(64) void ffn_logits_kernel(const bf16_t* __restrict__ x,
                                                         const bf16_t* __restrict__ wr, int T, int d,
                                                         int E, float* __restrict__ plog) {
   const int lane = threadIdx.x;
   const int q = lane >> 4, r16 = lane & 15;
-  const int tb = blockIdx.x, c = blockIdx.y, cls = blockIdx.z;
+  const int tb = blockIdx.x, c0 = blockIdx.y * TPW, cls = blockIdx.z;
   const int Tp = gridDim.x * kFfnTokens;
   const bf16_t* xr = x + (size_t)min(tb * kFfnTokens + r16, T - 1) * d + q * 8;
-  const bf16_t* br = wr + (size_t)min(c * 16 + r16, E - 1) * d + q * 8;
+  const bf16_t* br[TPW];
+#pragma unroll
+  for (int c = 0; c < TPW; ++c) br[c] = wr + (size_t)min((c0 + c) * 16 + r16, E - 1) * d + q * 8;
   const int nsteps = d / 32;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int c = 0; c < TPW; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   int s = cls;
   for (; s + 12 < nsteps; s += 16) {
-    Frag16 a[4], b[4];
+    Frag16 a[4], b[4][TPW];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       a[u].u = load16(xr + (s + 4 * u) * 32);
-      b[u].u = load16(br + (s + 4 * u) * 32);
+#pragma unroll
+      for (int c = 0; c < TPW; ++c) b[u][c].u = load16(br[c] + (s + 4 * u) * 32);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = mfma16x16x32(a[u].h, b[u].h, acc);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < TPW; ++c) acc[c] = mfma16x16x32(a[u].h, b[u][c].h, acc[c]);
   }
   for (; s < nsteps; s += 4) {
-    Frag16 a, b;
+    Frag16 a, b[TPW];
     a.u = load16(xr + s * 32);
-    b.u = load16(br + s * 32);
-    acc = mfma16x16x32(a.h, b.h, acc);
+#pragma unroll
+    for (int c = 0; c < TPW; ++c) b[c].u = load16(br[c] + s * 32);
+#pragma unroll
+    for (int c = 0; c < TPW; ++c) acc[c] = mfma16x16x32(a.h, b[c].h, acc[c]);
   }
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
-    plog[((size_t)cls * Tp + tb * kFfnTokens + q * 4 + v) * kMaxDispatchExperts + c * 16 + r16] = acc[v];
+  for (int c = 0; c < TPW; ++c)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      plog[((size_t)cls * Tp + tb * kFfnTokens + q * 4 + v) * kMaxDispatchExperts + (c0 + c) * 16 + r16] =
+          acc[c][v];
 }
 
 // Wave-wide maximum of a 64-bit key (h, l), returned in every lane: row
@@ -184,8 +199,12 @@ __global__ __launch_bounds__(kTopkThreads) void ffn_topk_kernel(const float* __r
 
 hipError_t launch_ffn_router(const RouterArgs& a, float* plog, hipStream_t stream) {
   const int tb = ceil_div(a.T, kFfnTokens);
-  ffn_logits_kernel<<<dim3(tb, ceil_div(a.E, 16), 4), 64, 0, stream>>>(a.x, a.wr, a.T, a.d, a.E,
-                                                                        plog);
+  const int tiles = ceil_div(a.E, 16);
+  if (a.T >= 1024)
+    ffn_logits_kernel<4><<<dim3(tb, ceil_div(tiles, 4), 4), 64, 0, stream>>>(a.x, a.wr, a.T, a.d,
+                                                                           a.E, plog);
+  else
+    ffn_logits_kernel<1><<<dim3(tb, tiles, 4), 64, 0, stream>>>(a.x, a.wr, a.T, a.d, a.E, plog);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   ffn_topk_kernel<<<tb, kTopkThreads, 0, stream>>>(plog, a.bias, a.T, a.E, a.k, a.scale, a.idx, a.w,

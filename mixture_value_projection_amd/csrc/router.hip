@@ -305,6 +305,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
+// Tokens per tile-router workgroup, measured on the value layer's shape with
+// the benchmark's inputs (the token rows are not cache-resident: a 32-token
+// tile is faster at T = 8192 only when they are).
 int router_tile_tokens(int T) { return T <= 8192 ? 16 : T <= 16384 ? 32 : 64; }
 
 hipError_t launch_router_tile(const RouterArgs& a, hipStream_t stream) {
