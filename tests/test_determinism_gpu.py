@@ -87,3 +87,61 @@ def test_graph_replay_matches_eager(T):
 def fwd_ws(g, ws, out=None):
     return binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], 4, 2.5, 8, 128,
                                  out=out, workspace=ws)
+
+
+def _layer(T, d, E, k, heads, hd, seed, mode):
+    shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=heads, head_dim=hd)
+    g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, seed, torch.bfloat16, "uniform").items()}
+    if mode == "ties":
+        # Experts 2j and 2j + 1 score alike: the lower index must rank first.
+        g["router_w"][1::2] = g["router_w"][0::2][: E // 2]
+        g["router_b"].zero_()
+    elif mode == "one_expert":
+        # Every token's first choice is expert E // 2 (all T tokens hit it).
+        g["router_b"][E // 2] = 50.0
+    return g
+
+
+def _run(g, k, heads, hd, env, monkeypatch):
+    for name, val in env.items():
+        monkeypatch.setenv(name, val)
+    T = g["x"].shape[0]
+    idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    out = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, 2.5, heads,
+                                hd, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    for name in env:
+        monkeypatch.delenv(name)
+    return out, idx, w
+
+
+@pytest.mark.parametrize("T,d,E,k,heads,hd,mode", [
+    (64, 2560, 64, 4, 8, 128, "uniform"),
+    (1, 512, 64, 4, 2, 128, "uniform"),
+    (5, 512, 16, 8, 1, 64, "uniform"),
+    (100, 512, 64, 1, 2, 128, "uniform"),
+    (256, 512, 64, 4, 2, 128, "uniform"),
+    (137, 512, 40, 6, 1, 128, "ties"),
+    (256, 512, 64, 4, 1, 128, "one_expert"),
+    (250, 1024, 7, 3, 1, 64, "one_expert"),
+])
+def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode, monkeypatch):
+    """The decode path (two-kernel router, weight-streaming experts) and the
+    grouped path (tile router, dispatch, grouped GEMM) give the same routing,
+    weights and output bits, also with tied scores and with every token on
+    one expert."""
+    g = _layer(T, d, E, k, heads, hd, seed=T + E, mode=mode)
+    print(f"paths T={T} d={d} E={E} k={k} N={heads * hd} {mode}", flush=True)
+    dec = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
+    grp = _run(g, k, heads, hd, {"MOVA_PATH": "grouped"}, monkeypatch)
+    for name, a, b in zip(("out", "idx", "w"), dec, grp):
+        assert torch.equal(a, b), f"{name}: decode path differs from the grouped path"
+    if mode == "ties":
+        # Experts 2j and 2j + 1 tie, so 2j + 1 is only ever taken after 2j.
+        for row in dec[1].cpu().tolist():
+            for pos, e in enumerate(row):
+                if e % 2 == 1:
+                    assert e - 1 in row[:pos], f"tie order broken in {row}"
+    if mode == "one_expert":
+        assert bool((dec[1][:, 0] == E // 2).all())
