@@ -145,3 +145,4 @@ def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode, monkeypat
                     assert e - 1 in row[:pos], f"tie order broken in {row}"
     if mode == "one_expert":
         assert bool((dec[1][:, 0] == E // 2).all())
+
