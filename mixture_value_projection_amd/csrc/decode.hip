@@ -1,4 +1,6 @@
-// Decode path: a weight-streaming kernel for small token counts.
+// Decode path: a weight-streaming kernel for small token counts, for the
+// value experts and, with other epilogues, the FFN experts' gate / up and down
+// projections (same products, same order, same bits as the grouped GEMM).
 //
 // With few tokens per expert the layer is bound by reading the touched
 // experts' weights (page "MoVA: routing the value vectors ...", section "So
@@ -46,11 +48,20 @@ constexpr int kGroups = 2;    // 16-column MFMA groups per wave
 // can, else 2, which always does since d % 64 == 0).  kPair32: experts with
 // more than 16 pairs use 32-pair passes (worth it beyond 64 tokens; without
 // it the kernel holds fewer registers, and such experts take 16-pair passes).
-template <int kUnroll, bool kPair32>
+//
+// kMode selects the epilogue, as in the grouped GEMM (GemmMode):
+//   kGemmRoutedSilu    partial[pair, n] = fp16(w * SiLU(z))     (value experts)
+//   kGemmRoutedSwiGLU  out_h[pair, c]   = bf16(SiLU(z_gate) * z_up)
+//                      (FFN gate / up: rows interleaved in blocks of 16, so a
+//                      wave's two column groups are one gate block and its
+//                      up block, and c = its first column / 2 + lane % 16)
+//   kGemmRoutedLinear  partial[pair, n] = fp16(w * z), A rows one per pair
+//                      (FFN down, A = the pairs' h rows)
+template <int kUnroll, bool kPair32, int kMode>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
-    f16_t* __restrict__ partial, int T, int d, int N, int E, int k) {
+    f16_t* __restrict__ partial, bf16_t* __restrict__ out_h, int T, int d, int N, int E, int k) {
   // An expert gets at most T * k pairs (k of them per token when a caller's
   // stored routing repeats an id; the router never does).
   __shared__ int plist[kDecodeMaxT * kMaxTopK];
@@ -124,8 +135,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     const bf16_t* xr[RG];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg)
-      xr[rg] = x + (size_t)(plist[min(p0 + rg * 16 + r16, ce - 1)] / k) * d + q * 8;
+    for (int rg = 0; rg < RG; ++rg) {
+      const int pr = plist[min(p0 + rg * 16 + r16, ce - 1)];
+      xr[rg] = x + (size_t)(kMode == kGemmRoutedLinear ? pr : pr / k) * d + q * 8;
+    }
     auto load_x = [&](Frag16 (&f)[RG][kUnroll], int bt) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg)
@@ -172,11 +185,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int v = 0; v < 4; ++v) {
         const int r = p0 + rg * 16 + q * 4 + v;
         if (r < ce) {
-          const float wt = wlist[r];
-          f16_t* dst = partial + (size_t)plist[r] * N;
+          if constexpr (kMode == kGemmRoutedSwiGLU) {
+            // Group 0 is the gate block, group 1 its up block (N % 32 == 0).
+            bf16_t* dst = out_h + (size_t)plist[r] * (N / 2);
+            if (ncol[0] < N)
+              dst[(ncol[0] - r16) / 2 + r16] = (bf16_t)(siluf(acc[rg][0][v]) * acc[rg][1][v]);
+          } else {
+            const float wt = wlist[r];
+            f16_t* dst = partial + (size_t)plist[r] * N;
 #pragma unroll
-          for (int g = 0; g < kGroups; ++g)
-            if (ncol[g] < N) dst[ncol[g]] = (f16_t)(wt * siluf(acc[rg][g][v]));
+            for (int g = 0; g < kGroups; ++g) {
+              if (ncol[g] < N) {
+                const float z = acc[rg][g][v];
+                if constexpr (kMode == kGemmRoutedSilu) dst[ncol[g]] = (f16_t)(wt * siluf(z));
+                else dst[ncol[g]] = (f16_t)(wt * z);
+              }
+            }
+          }
         }
       }
     }
@@ -190,14 +215,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+template <int kMode>
+static hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.E * ceil_div(a.N, kSlice));
   const bool unroll4 = (a.d / 32) % 4 == 0;
   const bool pair32 = a.T > 64;
-  auto kern = unroll4 ? (pair32 ? decode_kernel<4, true> : decode_kernel<4, false>)
-                      : (pair32 ? decode_kernel<2, true> : decode_kernel<2, false>);
-  kern<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N, a.E, a.k);
+  auto kern = unroll4 ? (pair32 ? decode_kernel<4, true, kMode> : decode_kernel<4, false, kMode>)
+                      : (pair32 ? decode_kernel<2, true, kMode> : decode_kernel<2, false, kMode>);
+  kern<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, (bf16_t*)a.out_h, a.T, a.d,
+                                 a.N, a.E, a.k);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.T > kDecodeMaxT || a.k > kMaxTopK || a.d % 64 != 0 || a.N % 64 != 0)
+    return hipErrorInvalidValue;
+  switch (a.mode) {
+    case kGemmRoutedSilu: return launch_decode_mode<kGemmRoutedSilu>(a, stream);
+    case kGemmRoutedSwiGLU:
+      if (a.N % 32 != 0 || a.out_h == nullptr) return hipErrorInvalidValue;
+      return launch_decode_mode<kGemmRoutedSwiGLU>(a, stream);
+    case kGemmRoutedLinear: return launch_decode_mode<kGemmRoutedLinear>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace mova

@@ -112,12 +112,17 @@ size_t dense_skinny_partial_floats(int T, int d, int N);
 hipError_t launch_dense_skinny(const DenseArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
-  const __bf16* x;
-  const __bf16* W;
+  const __bf16* x;      // A rows: tokens [T, d], or (kGemmRoutedLinear) one row per pair [T * k, d]
+  const __bf16* W;      // [E, N, d]
   const int32_t* idx;   // [T, k]
   const float* topk_w;  // [T, k]
-  f16_t* partial;       // [T * k, N]
+  f16_t* partial;       // [T * k, N] (kGemmRoutedSilu, kGemmRoutedLinear)
   int T, d, N, E, k;
+  // Epilogue, as the grouped GEMM's mode of the same name: kGemmRoutedSilu,
+  // kGemmRoutedSwiGLU (gate / up rows interleaved in blocks of 16, writes
+  // out_h[pair, N / 2] bf16) or kGemmRoutedLinear.
+  int mode = kGemmRoutedSilu;
+  __bf16* out_h = nullptr;
 };
 // The decode path handles at most this many tokens per call.
 constexpr int kDecodeMaxT = 256;

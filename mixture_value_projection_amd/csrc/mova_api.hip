@@ -468,8 +468,9 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
     err = launch_ffn_router(ra, (float*)(ws + L.plog), stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
+  const bool decode = choose_path(T, k) == Path::Decode;
   const GemmTile tile = gemm_tile_grouped(T, k, E);
-  {
+  if (!decode) {
     StageScope sc(1, stream);
     DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, ffn_router_chunk_tokens(), tile.bm};
     err = launch_dispatch(dp, stream);
@@ -479,13 +480,27 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
     StageScope sc(2, stream);
     // Routed experts: h[pair] = SiLU(gate x) * (up x), then partial[pair] =
     // w * (down h); the shared expert the same on every token, unweighted.
-    GemmArgs gu{xb, (const __bf16*)gate_up_w, perm, w, eoff, tbase, nullptr, h,
-                T, d, 2 * inter, E, k, tile, kGemmRoutedSwiGLU};
-    err = launch_grouped_gemm(gu, stream);
-    if (err == hipSuccess) {
-      GemmArgs dn{h, (const __bf16*)down_w, perm, w, eoff, tbase, partial, nullptr,
-                  T, inter, d, E, k, tile, kGemmRoutedLinear};
-      err = launch_grouped_gemm(dn, stream);
+    // Few tokens: the weight-streaming decode kernel, which finds each
+    // expert's pairs itself (no dispatch); else the grouped GEMM.
+    if (decode) {
+      DecodeArgs gu{xb, (const __bf16*)gate_up_w, idx, w, nullptr, T, d, 2 * inter, E, k};
+      gu.mode = kGemmRoutedSwiGLU;
+      gu.out_h = h;
+      err = launch_decode(gu, stream);
+      if (err == hipSuccess) {
+        DecodeArgs dn{h, (const __bf16*)down_w, idx, w, partial, T, inter, d, E, k};
+        dn.mode = kGemmRoutedLinear;
+        err = launch_decode(dn, stream);
+      }
+    } else {
+      GemmArgs gu{xb, (const __bf16*)gate_up_w, perm, w, eoff, tbase, nullptr, h,
+                  T, d, 2 * inter, E, k, tile, kGemmRoutedSwiGLU};
+      err = launch_grouped_gemm(gu, stream);
+      if (err == hipSuccess) {
+        GemmArgs dn{h, (const __bf16*)down_w, perm, w, eoff, tbase, partial, nullptr,
+                    T, inter, d, E, k, tile, kGemmRoutedLinear};
+        err = launch_grouped_gemm(dn, stream);
+      }
     }
     if (err == hipSuccess && inter_shared > 0 && T <= kDenseSkinnyMaxT) {
       // Few tokens: the weight-streaming split-k kernel, whose reduction

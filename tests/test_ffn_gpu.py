@@ -124,3 +124,26 @@ def test_ffn_rows_do_not_depend_on_other_tokens():
     assert torch.equal(full[123:323], part)
     again, _, _ = run_ffn(g, sh)
     assert torch.equal(full, again)
+
+
+@pytest.mark.parametrize("T,d,E,k,inter,inter_s", [
+    (64, 2560, 100, 8, 768, 768),
+    (1, 256, 12, 3, 64, 64),
+    (256, 192, 128, 8, 64, 128),   # d % 128 != 0: half a column slice in the down projection
+    (100, 512, 100, 8, 128, 0),
+    (200, 128, 1, 1, 64, 64),      # every token on one expert: 200 pairs, passes of 32
+])
+def test_ffn_decode_and_grouped_paths_bitwise(T, d, E, k, inter, inter_s, monkeypatch):
+    """Few tokens take the weight-streaming decode kernel for the routed
+    experts; forcing the grouped GEMM instead gives the same bits."""
+    sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s,
+                         scale=1.0 if k == 1 else 2.5)
+    say(f"ffn paths T={T} d={d} E={E} k={k} inter={inter} shared={inter_s}")
+    L, g = gpu_layer(sh, seed=T + 7 * E)
+    res = {}
+    for path in ("decode", "grouped"):
+        monkeypatch.setenv("MOVA_PATH", path)
+        res[path] = run_ffn(g, sh)
+    monkeypatch.delenv("MOVA_PATH")
+    for name, a, b in zip(("out", "idx", "w"), res["decode"], res["grouped"]):
+        assert torch.equal(a, b), f"{name}: decode path differs from the grouped path"
