@@ -160,6 +160,55 @@ FfnLayout ffn_layout(int T, int d, int E, int k, int inter, int inter_shared) {
 
 // ---- stage timing -------------------------------------------------------
 constexpr int kStages = 5;
+// Library-owned side stream of a device, for work that depends only on the
+// call's inputs and can overlap the rest of the call (the FFN's shared
+// expert).  It is forked from the caller's stream with an event and joined
+// back with another before the results meet, so the call stays ordered on
+// the caller's stream as a whole, also under graph capture.  Default
+// priority, non-blocking; created on the device's first use and kept until
+// the process ends.  The events are reused by every call, so forks and joins
+// are enqueued under g_side_mu (enqueueing only: the work itself overlaps).
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+std::vector<SideStream> g_side;  // by device
+
+// The side stream for work ordered after `stream`, or null (run on `stream`
+// itself): MOVA_SERIAL=1, a stream of another device than the current one,
+// a first use while `stream` is capturing, or a failure to create the
+// stream.  Call with g_side_mu held.
+SideStream* side_stream_for(hipStream_t stream) {
+  const char* serial = getenv("MOVA_SERIAL");
+  if (serial != nullptr && strcmp(serial, "1") == 0) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || (int)sdev != dev) return nullptr;
+  }
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
+  SideStream& ss = g_side[dev];
+  if (ss.s == nullptr) {
+    // No stream creation while the caller's stream is being captured (it
+    // may invalidate the capture): such a first call runs serially.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+      return nullptr;
+    SideStream fresh;
+    if (hipStreamCreateWithFlags(&fresh.s, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&fresh.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&fresh.join, hipEventDisableTiming) != hipSuccess) {
+      if (fresh.fork != nullptr) (void)hipEventDestroy(fresh.fork);
+      (void)hipStreamDestroy(fresh.s);
+      return nullptr;
+    }
+    ss = fresh;
+  }
+  return &ss;
+}
+
 struct Timing {
   std::mutex mu;
   int capacity = 0;
@@ -461,7 +510,65 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
   __bf16* hs = (__bf16*)(ws + L.hs);
   f16_t* ps = (f16_t*)(ws + L.ps);
   const __bf16* xb = (const __bf16*)x;
-  hipError_t err;
+  hipError_t err = hipSuccess;
+
+  // The shared expert depends on x alone: it runs first, on the side stream
+  // when there is one, overlapping the router and the routed experts.  Its
+  // buffers (hs, ps, sk) are its own.
+  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+  SideStream* side = nullptr;
+  if (inter_shared > 0) {
+    side_lock.lock();
+    side = side_stream_for(stream);
+    if (side == nullptr) side_lock.unlock();
+  }
+  bool joined = side == nullptr;
+  auto join = [&]() {  // the caller's stream waits for the shared expert
+    if (joined) return hipSuccess;
+    joined = true;
+    const hipError_t e = hipStreamWaitEvent(stream, side->join, 0);
+    side_lock.unlock();
+    return e;
+  };
+  struct JoinAtExit {
+    decltype(join)& f;
+    ~JoinAtExit() { (void)f(); }
+  } join_at_exit{join};
+  if (inter_shared > 0) {
+    hipStream_t ss = stream;
+    if (side != nullptr) {
+      err = hipEventRecord(side->fork, stream);
+      if (err == hipSuccess) err = hipStreamWaitEvent(side->s, side->fork, 0);
+      ss = side->s;
+    }
+    if (err == hipSuccess && T <= kDenseSkinnyMaxT) {
+      // Few tokens: the weight-streaming split-k kernel, whose reduction
+      // applies the SwiGLU (gate/up) or rounds to fp16 (down).
+      float* sk = (float*)(ws + L.sk);
+      DenseArgs sg{xb, (const __bf16*)shared_gate_up_w, sk, nullptr, T, d, 2 * inter_shared,
+                   kDenseOutSwiGLU, hs};
+      err = launch_dense_skinny(sg, ss);
+      if (err == hipSuccess) {
+        DenseArgs sd{hs, (const __bf16*)shared_down_w, sk, nullptr, T, inter_shared, d,
+                     kDenseOutF16, ps};
+        err = launch_dense_skinny(sd, ss);
+      }
+    } else if (err == hipSuccess) {
+      GemmArgs sg{xb, (const __bf16*)shared_gate_up_w, nullptr, nullptr, nullptr, nullptr,
+                  nullptr, hs, T, d, 2 * inter_shared, 1, 1, {0, 0, 0, 0}, kGemmDenseSwiGLU};
+      err = launch_dense_gemm(sg, ss);
+      if (err == hipSuccess) {
+        GemmArgs sd{hs, (const __bf16*)shared_down_w, nullptr, nullptr, nullptr, nullptr, ps,
+                    nullptr, T, inter_shared, d, 1, 1, {0, 0, 0, 0}, kGemmDenseF16};
+        err = launch_dense_gemm(sd, ss);
+      }
+    }
+    if (side != nullptr) {
+      const hipError_t e = hipEventRecord(side->join, side->s);
+      if (err == hipSuccess) err = e;
+    }
+  }
+  if (err != hipSuccess) return MOVA_ERR_HIP;
   {
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w, chunk};
@@ -479,8 +586,7 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
   {
     StageScope sc(2, stream);
     // Routed experts: h[pair] = SiLU(gate x) * (up x), then partial[pair] =
-    // w * (down h); the shared expert the same on every token, unweighted.
-    // Few tokens: the weight-streaming decode kernel, which finds each
+    // w * (down h).  Few tokens: the weight-streaming decode kernel, which finds each
     // expert's pairs itself (no dispatch); else the grouped GEMM.
     if (decode) {
       DecodeArgs gu{xb, (const __bf16*)gate_up_w, idx, w, nullptr, T, d, 2 * inter, E, k};
@@ -502,29 +608,8 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
         err = launch_grouped_gemm(dn, stream);
       }
     }
-    if (err == hipSuccess && inter_shared > 0 && T <= kDenseSkinnyMaxT) {
-      // Few tokens: the weight-streaming split-k kernel, whose reduction
-      // applies the SwiGLU (gate/up) or rounds to fp16 (down).
-      float* sk = (float*)(ws + L.sk);
-      DenseArgs sg{xb, (const __bf16*)shared_gate_up_w, sk, nullptr, T, d, 2 * inter_shared,
-                   kDenseOutSwiGLU, hs};
-      err = launch_dense_skinny(sg, stream);
-      if (err == hipSuccess) {
-        DenseArgs sd{hs, (const __bf16*)shared_down_w, sk, nullptr, T, inter_shared, d,
-                     kDenseOutF16, ps};
-        err = launch_dense_skinny(sd, stream);
-      }
-    } else if (err == hipSuccess && inter_shared > 0) {
-      GemmArgs sg{xb, (const __bf16*)shared_gate_up_w, nullptr, nullptr, nullptr, nullptr,
-                  nullptr, hs, T, d, 2 * inter_shared, 1, 1, {0, 0, 0, 0}, kGemmDenseSwiGLU};
-      err = launch_dense_gemm(sg, stream);
-      if (err == hipSuccess) {
-        GemmArgs sd{hs, (const __bf16*)shared_down_w, nullptr, nullptr, nullptr, nullptr, ps,
-                    nullptr, T, inter_shared, d, 1, 1, {0, 0, 0, 0}, kGemmDenseF16};
-        err = launch_dense_gemm(sd, stream);
-      }
-    }
   }
+  if (err == hipSuccess) err = join();
   if (err != hipSuccess) return MOVA_ERR_HIP;
   {
     StageScope sc(3, stream);

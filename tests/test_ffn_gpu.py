@@ -147,3 +147,46 @@ def test_ffn_decode_and_grouped_paths_bitwise(T, d, E, k, inter, inter_s, monkey
     monkeypatch.delenv("MOVA_PATH")
     for name, a, b in zip(("out", "idx", "w"), res["decode"], res["grouped"]):
         assert torch.equal(a, b), f"{name}: decode path differs from the grouped path"
+
+
+@pytest.mark.parametrize("T", [64, 600])
+def test_ffn_shared_expert_side_stream(T, monkeypatch):
+    """The shared expert runs on the library's side stream, overlapping the
+    router and the routed experts; the result is the bits of running it on
+    the caller's stream (MOVA_SERIAL=1), also when the call is captured in a
+    graph and replayed with other work in between."""
+    sh = inputs.FfnShape(T=T, d=512, E=100, k=8, inter=128, inter_shared=256)
+    say(f"ffn side stream T={T}")
+    L, g = gpu_layer(sh, seed=T + 1)
+    monkeypatch.setenv("MOVA_SERIAL", "1")
+    serial = run_ffn(g, sh)
+    monkeypatch.delenv("MOVA_SERIAL")
+    side = run_ffn(g, sh)
+    for name, a, b in zip(("out", "idx", "w"), side, serial):
+        assert torch.equal(a, b), f"{name}: side stream changed the result"
+    # Graph capture of the forked call, replayed with eager calls between.
+    ws = torch.empty(binding.ffn_workspace_bytes(T, sh.d, sh.E, sh.k, sh.inter, sh.inter_shared),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty(T, sh.d, dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        binding.ffn_moe_forward(g["x"], g["router_w"], g["router_b"], g["gate_up_w"],
+                                g["down_w"], sh.k, sh.scale, g["shared_gate_up_w"],
+                                g["shared_down_w"], out=out, workspace=ws)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(4):
+        out.zero_()
+        other = run_ffn(g, sh, g["x"][: T // 2].contiguous())   # eager work in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, serial[0]), f"replay {rep} differs"
+        del other
