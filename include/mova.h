@@ -209,7 +209,9 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
                           hipStream_t stream);
 
 /*
- * FFN mixture of experts on the same dispatch and tiled-GEMM kernels: the
+ * FFN mixture of experts on the same kernels as the value path (the
+ * weight-streaming decode kernel for T <= 256, else dispatch and the tiled
+ * GEMM; both give the same bits): the
  * sparse FFN the model runs beside its routed value projection, 100 experts
  * with top-8 routing plus one shared expert (the thevalue.engineering page
  * on the MoVA architecture, section "Dual sparsity").  The pages give neither
@@ -240,6 +242,16 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
  * are fp32: four MFMA chains per (token, expert) over the k steps of each
  * residue class mod 4, in order, added in class order.  Errors as for
  * mova_value_forward.
+ * Streams: the shared expert depends on x alone and runs on a stream the
+ * library owns for the current device (created on first use, default
+ * priority, kept until the process ends), forked from `stream` with an event
+ * at the start of the call and joined back before the results are combined.
+ * The call is therefore ordered on `stream` as a whole, also when `stream` is
+ * being captured into a graph.  The side stream is not used when `stream`
+ * belongs to another device than the current one, when its first use would
+ * fall inside a capture, or when the environment sets MOVA_SERIAL=1.  Calls
+ * from several host threads are safe; their shared experts share the one
+ * side stream.
  */
 size_t mova_ffn_workspace_bytes(int T, int d, int E, int k, int inter, int inter_shared);
 
