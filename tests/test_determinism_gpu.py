@@ -146,3 +146,4 @@ def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode, monkeypat
     if mode == "one_expert":
         assert bool((dec[1][:, 0] == E // 2).all())
 
+
