@@ -210,8 +210,8 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
 
 /*
  * FFN mixture of experts on the same kernels as the value path (the
- * weight-streaming decode kernel for T <= 256, else dispatch and the tiled
- * GEMM; both give the same bits): the
+ * weight-streaming decode kernel up to T * k = 1024 pairs, else dispatch and
+ * the tiled GEMM; both give the same bits): the
  * sparse FFN the model runs beside its routed value projection, 100 experts
  * with top-8 routing plus one shared expert (the thevalue.engineering page
  * on the MoVA architecture, section "Dual sparsity").  The pages give neither

@@ -55,6 +55,20 @@ Path choose_path(int T, int k) {
   return (T <= kDecodeAutoMaxT && decode_ok) ? Path::Decode : Path::Grouped;
 }
 
+// The FFN's routed experts take the decode kernel up to 1024 pairs (T = 128
+// at k = 8): measured at d = 2560, 100 experts of width 768, it is faster at
+// T = 64, level at 128 and slower from 192 on, where the experts average more
+// than 15 pairs.  MOVA_PATH forces either path, as for the value path.
+Path choose_ffn_path(int T, int k) {
+  const char* force = getenv("MOVA_PATH");
+  const bool decode_ok = T <= kDecodeMaxT;
+  if (force != nullptr) {
+    if (strcmp(force, "decode") == 0 && decode_ok) return Path::Decode;
+    if (strcmp(force, "grouped") == 0) return Path::Grouped;
+  }
+  return (decode_ok && (long long)T * k <= 1024) ? Path::Decode : Path::Grouped;
+}
+
 // Workspace layout (every region 256-byte aligned):
 //   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] i32 |
 //   tile_base [E+1] i32 | plog (small-T router partial logits, T <= kDecodeMaxT
@@ -208,6 +222,53 @@ SideStream* side_stream_for(hipStream_t stream) {
   }
   return &ss;
 }
+
+// One fork of side-stream work off the caller's stream, in three steps:
+// begin() records the fork on the caller's stream and hands out the stream
+// to launch on (the side stream, or the caller's own when there is none),
+// end() records the join on it, join() makes the caller's stream wait for
+// it.  join() also runs on destruction, so an early return never leaves the
+// caller's stream (or a graph being captured) un-joined.  The side stream's
+// lock is held from construction to the join.
+class SideFork {
+ public:
+  SideFork(hipStream_t stream, bool wanted) : stream_(stream), lock_(g_side_mu, std::defer_lock) {
+    if (!wanted) return;
+    lock_.lock();
+    side_ = side_stream_for(stream);
+    if (side_ == nullptr) lock_.unlock();
+  }
+  SideFork(const SideFork&) = delete;
+  SideFork& operator=(const SideFork&) = delete;
+  ~SideFork() { (void)join(); }
+
+  hipError_t begin(hipStream_t* launch_stream) {
+    *launch_stream = stream_;
+    if (side_ == nullptr) return hipSuccess;
+    forked_ = true;
+    hipError_t e = hipEventRecord(side_->fork, stream_);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side_->s, side_->fork, 0);
+    *launch_stream = side_->s;
+    return e;
+  }
+  hipError_t end() {
+    return forked_ ? hipEventRecord(side_->join, side_->s) : hipSuccess;
+  }
+  hipError_t join() {
+    if (side_ == nullptr) return hipSuccess;
+    hipError_t e = hipSuccess;
+    if (forked_) e = hipStreamWaitEvent(stream_, side_->join, 0);
+    side_ = nullptr;
+    lock_.unlock();
+    return e;
+  }
+
+ private:
+  hipStream_t stream_;
+  std::unique_lock<std::mutex> lock_;
+  SideStream* side_ = nullptr;
+  bool forked_ = false;
+};
 
 struct Timing {
   std::mutex mu;
@@ -515,32 +576,10 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
   // The shared expert depends on x alone: it runs first, on the side stream
   // when there is one, overlapping the router and the routed experts.  Its
   // buffers (hs, ps, sk) are its own.
-  std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-  SideStream* side = nullptr;
-  if (inter_shared > 0) {
-    side_lock.lock();
-    side = side_stream_for(stream);
-    if (side == nullptr) side_lock.unlock();
-  }
-  bool joined = side == nullptr;
-  auto join = [&]() {  // the caller's stream waits for the shared expert
-    if (joined) return hipSuccess;
-    joined = true;
-    const hipError_t e = hipStreamWaitEvent(stream, side->join, 0);
-    side_lock.unlock();
-    return e;
-  };
-  struct JoinAtExit {
-    decltype(join)& f;
-    ~JoinAtExit() { (void)f(); }
-  } join_at_exit{join};
+  SideFork fork(stream, inter_shared > 0);
   if (inter_shared > 0) {
     hipStream_t ss = stream;
-    if (side != nullptr) {
-      err = hipEventRecord(side->fork, stream);
-      if (err == hipSuccess) err = hipStreamWaitEvent(side->s, side->fork, 0);
-      ss = side->s;
-    }
+    err = fork.begin(&ss);
     if (err == hipSuccess && T <= kDenseSkinnyMaxT) {
       // Few tokens: the weight-streaming split-k kernel, whose reduction
       // applies the SwiGLU (gate/up) or rounds to fp16 (down).
@@ -563,10 +602,8 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
         err = launch_dense_gemm(sd, ss);
       }
     }
-    if (side != nullptr) {
-      const hipError_t e = hipEventRecord(side->join, side->s);
-      if (err == hipSuccess) err = e;
-    }
+    const hipError_t e = fork.end();
+    if (err == hipSuccess) err = e;
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
   {
@@ -575,7 +612,7 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
     err = launch_ffn_router(ra, (float*)(ws + L.plog), stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
-  const bool decode = choose_path(T, k) == Path::Decode;
+  const bool decode = choose_ffn_path(T, k) == Path::Decode;
   const GemmTile tile = gemm_tile_grouped(T, k, E);
   if (!decode) {
     StageScope sc(1, stream);
@@ -609,7 +646,7 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
       }
     }
   }
-  if (err == hipSuccess) err = join();
+  if (err == hipSuccess) err = fork.join();
   if (err != hipSuccess) return MOVA_ERR_HIP;
   {
     StageScope sc(3, stream);

@@ -190,3 +190,44 @@ def test_ffn_shared_expert_side_stream(T, monkeypatch):
         torch.cuda.synchronize()
         assert torch.equal(out, serial[0]), f"replay {rep} differs"
         del other
+
+
+def test_ffn_concurrent_host_threads():
+    """Two host threads call the FFN on their own streams and workspaces (their
+    shared experts share the library's side stream): every result matches the
+    same call made alone."""
+    import threading
+    sh = inputs.FfnShape(T=64, d=512, E=100, k=8, inter=128, inter_shared=256)
+    L, g = gpu_layer(sh, seed=5)
+    xs = [g["x"], inputs.make_tokens(sh.T, sh.d, 77, torch.bfloat16).to(DEV)]
+    refs = [run_ffn(g, sh, x)[0].clone() for x in xs]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            ws = torch.empty(binding.ffn_workspace_bytes(sh.T, sh.d, sh.E, sh.k, sh.inter,
+                                                         sh.inter_shared),
+                             dtype=torch.uint8, device=DEV)
+            out = torch.empty(sh.T, sh.d, dtype=torch.bfloat16, device=DEV)
+            for rep in range(20):
+                with torch.cuda.stream(s):
+                    out.zero_()
+                    binding.ffn_moe_forward(xs[i], g["router_w"], g["router_b"], g["gate_up_w"],
+                                            g["down_w"], sh.k, sh.scale, g["shared_gate_up_w"],
+                                            g["shared_down_w"], out=out, workspace=ws)
+                s.synchronize()
+                if not torch.equal(out, refs[i]):
+                    errors.append(f"thread {i} rep {rep} differs")
+                    return
+        except Exception as exc:  # reported below
+            errors.append(f"thread {i}: {exc!r}")
+
+    say("ffn two host threads")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
