@@ -20,8 +20,14 @@
 //                          selection (lane = token) and the per-chunk
 //                          dispatch histogram in the same kernel (large T,
 //                          and routing-only calls);
+//   router_staged_kernel   one workgroup per 32 or 64 tokens, the router
+//                          weight staged through LDS once per workgroup and
+//                          shared by its 8 or 16 waves (mid-size T);
 //   router_partial_kernel  + router_topk_kernel: the same chains spread over
 //                          single-wave workgroups for small T.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -130,6 +136,88 @@ __device__ __forceinline__ void insert_ranked(float (&bv)[KK], float (&bs)[KK], 
   }
 }
 
+// Selection with lane = token for a tile of TM <= 64 tokens whose class
+// partials sit in part[4][TM][kMaxExperts + 1]: wave w < 4 keeps each token's
+// top-k over experts 16w .. 16w + 15 (offered in index order), and wave 0
+// merges the other three waves' lists in wave order -- the same selection,
+// order and weight sum as topk_tokens.  Every thread of the workgroup calls
+// it (it holds a barrier); waves past 3 only take part in the barrier.  bq:
+// the biases of the wave's 16 experts (load_selection_bias).  Writes rows
+// t0 .. t0 + TM - 1 (those below T) of idx / w, and counts the selected
+// experts into hist when it is not null.
+constexpr int kSelQ = kMaxExperts / 4;  // experts per selecting wave
+
+__device__ __forceinline__ void load_selection_bias(const float* __restrict__ bias, int wave, int E,
+                                                    float (&bq)[kSelQ]) {
+  const int wq = __builtin_amdgcn_readfirstlane(wave & 3);  // wave-uniform: scalar loads
+#pragma unroll
+  for (int j = 0; j < kSelQ; ++j) bq[j] = (bias != nullptr && wq * kSelQ + j < E) ? bias[wq * kSelQ + j] : 0.f;
+}
+
+template <int TM, int KK>
+__device__ __forceinline__ void select_lane_token(
+    const float (*part)[TM][kMaxExperts + 1], float (*cand_v)[KK][TM], float (*cand_s)[KK][TM],
+    int (*cand_i)[KK][TM], int wave, int lane, const float (&bq)[kSelQ], int E, int k,
+    float scale, int t0, int T, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+    int* hist) {
+  constexpr int kQ = kSelQ;
+  float bv[KK], bs[KK];
+  int bi[KK];
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+    bv[j] = -__builtin_inff();
+    bs[j] = 0.f;
+    bi[j] = 0;
+  }
+  if (wave < 4 && lane < TM) {
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      const int e = wave * kQ + j;
+      if (e < E) {
+        const float logit =
+            ((part[0][lane][e] + part[1][lane][e]) + part[2][lane][e]) + part[3][lane][e];
+        const float sc = sigmoidf_fast(logit);
+        insert_ranked<KK>(bv, bs, bi, k, sc + bq[j], sc, e);
+      }
+    }
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        cand_v[wave - 1][j][lane] = bv[j];
+        cand_s[wave - 1][j][lane] = bs[j];
+        cand_i[wave - 1][j][lane] = bi[j];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < TM) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int j = 0; j < KK; ++j)
+        if (j < k)
+          insert_ranked<KK>(bv, bs, bi, k, cand_v[w][j][lane], cand_s[w][j][lane], cand_i[w][j][lane]);
+    float ssum = 0.f;
+#pragma unroll
+    for (int j = 0; j < KK; ++j)
+      if (j < k) ssum += bs[j];
+    const int t = t0 + lane;
+    if (t < T) {
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        if (j < k) {
+          // Clamped so that even non-finite scores (undefined results) can
+          // never produce an out-of-range expert index.
+          const int e = min(max(bi[j], 0), E - 1);
+          idx_out[(size_t)t * k + j] = e;
+          w_out[(size_t)t * k + j] = scale * bs[j] / ssum;
+          if (hist != nullptr) atomicAdd(&hist[e], 1);
+        }
+      }
+    }
+  }
+}
+
 // ---- tile router: one workgroup per 16 * TG tokens ------------------------
 //
 // Wave rc (of 4) runs class rc's chains for all TG token groups against all
@@ -150,7 +238,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     int T, int d, int E, int k, float scale,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts) {
   constexpr int TM = 16 * TG;
-  constexpr int kQ = kMaxExperts / 4;       // experts per wave in the selection
   constexpr int kPad = kMaxExperts + 1;
   __shared__ float part[4][TM][kPad];
   constexpr bool kLaneToken = TG > 1;        // selection with lane = token
@@ -167,11 +254,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int t0 = blockIdx.x * TM;
 
   if (threadIdx.x < kMaxExperts) hist[threadIdx.x] = 0;
-  // Biases of this wave's selection experts (wave-uniform: scalar loads).
-  const int wq = __builtin_amdgcn_readfirstlane(rc);
-  float bq[kQ];
-#pragma unroll
-  for (int j = 0; j < kQ; ++j) bq[j] = (bias != nullptr && wq * kQ + j < E) ? bias[wq * kQ + j] : 0.f;
+  // Biases of this wave's selection experts.
+  float bq[kSelQ];
+  load_selection_bias(bias, rc, E, bq);
   // Token rows clamped into range (rows past T are never written); expert rows
   // clamped (experts >= E are never offered to the selection).
   const bf16_t* xrow[TG];
@@ -243,61 +328,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
   } else {
     // Larger tiles: lane = token (row `lane` of the tile).
-    float bv[KK], bs[KK];
-    int bi[KK];
-#pragma unroll
-    for (int j = 0; j < KK; ++j) {
-      bv[j] = -__builtin_inff();
-      bs[j] = 0.f;
-      bi[j] = 0;
-    }
-    if (lane < TM) {
-#pragma unroll
-      for (int j = 0; j < kQ; ++j) {
-        const int e = wq * kQ + j;
-        if (e < E) {
-          const float logit =
-              ((part[0][lane][e] + part[1][lane][e]) + part[2][lane][e]) + part[3][lane][e];
-          const float sc = sigmoidf_fast(logit);
-          insert_ranked<KK>(bv, bs, bi, k, sc + bq[j], sc, e);
-        }
-      }
-      if (rc > 0) {
-#pragma unroll
-        for (int j = 0; j < KK; ++j) {
-          cand_v[rc - 1][j][lane] = bv[j];
-          cand_s[rc - 1][j][lane] = bs[j];
-          cand_i[rc - 1][j][lane] = bi[j];
-        }
-      }
-    }
-    __syncthreads();
-    if (rc == 0 && lane < TM) {
-#pragma unroll
-      for (int w = 0; w < 3; ++w)
-#pragma unroll
-        for (int j = 0; j < KK; ++j)
-          if (j < k)
-            insert_ranked<KK>(bv, bs, bi, k, cand_v[w][j][lane], cand_s[w][j][lane], cand_i[w][j][lane]);
-      float ssum = 0.f;
-#pragma unroll
-      for (int j = 0; j < KK; ++j)
-        if (j < k) ssum += bs[j];
-      const int t = t0 + lane;
-      if (t < T) {
-#pragma unroll
-        for (int j = 0; j < KK; ++j) {
-          if (j < k) {
-            // Clamped so that even non-finite scores (undefined results) can
-            // never produce an out-of-range expert index.
-            const int e = min(max(bi[j], 0), E - 1);
-            idx_out[(size_t)t * k + j] = e;
-            w_out[(size_t)t * k + j] = scale * bs[j] / ssum;
-            if (chunk_counts != nullptr) atomicAdd(&hist[e], 1);
-          }
-        }
-      }
-    }
+    select_lane_token<TM, KK>(part, cand_v, cand_s, cand_i, rc, lane, bq, E, k, scale, t0, T,
+                              idx_out, w_out, chunk_counts != nullptr ? hist : nullptr);
   }
   if (chunk_counts != nullptr) {
     __syncthreads();
@@ -305,14 +337,194 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
 }
 
-// Tokens per tile-router workgroup, measured on the value layer's shape with
-// the benchmark's inputs (the token rows are not cache-resident: a 32-token
-// tile is faster at T = 8192 only when they are).
-int router_tile_tokens(int T) { return T <= 8192 ? 16 : T <= 16384 ? 32 : 64; }
+// ---- staged-weight router: one workgroup per TM = 32 or 64 tokens --------
+//
+// The tile router's workgroups each read the whole router weight (d * E * 2
+// bytes) from L2 for their 16 .. 64 tokens, and that read, not the tokens,
+// sets its time at large T.  Here the weight goes through LDS once per
+// workgroup and is shared by 4 * TM / 16 waves: wave w runs class rc = w % 4's
+// chains for token group g = w / 4 against all four expert blocks.  The
+// weight arrives in chunks of 8 k steps (all 64 expert rows, 32 KB): thread
+// slots copy 16-byte pieces global -> registers -> LDS, kChunksAhead chunks
+// ahead in registers, into two LDS buffers with one barrier per chunk; the
+// token fragments (two per chunk per wave: steps 8j + rc and 8j + 4 + rc) are
+// read straight from global memory the same number of chunks ahead.  Every
+// chain adds the same products in the same order as the tile router's, so
+// the logits, and everything after them, have the same bits.  Staged rows are
+// 512 B; the 16-byte piece c of row r sits at c ^ (r & 7), so the 16 rows a
+// fragment read touches fall in distinct bank groups.
+constexpr int kStageSteps = 8;                                // k steps per staged chunk
+constexpr int kStageRowBytes = kStageSteps * 32 * 2;          // 512 B per expert row
+constexpr int kStageBytes = kMaxExperts * kStageRowBytes;     // 32 KB per chunk
+constexpr int kChunksAhead = 3;
+
+template <int TM, int KK>
+__global__ __launch_bounds__(4 * TM * 4) void router_staged_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
+    int T, int d, int E, int k, float scale,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts) {
+  constexpr int kGroupsT = TM / 16;
+  constexpr int kThreads = 64 * 4 * kGroupsT;
+  constexpr int kPieces = kStageBytes / 16 / kThreads;  // 16-byte pieces per thread per chunk
+  constexpr int kPad = kMaxExperts + 1;
+  // The class partials are written only after the k loop, into the memory
+  // of the weight buffers (32-token tiles then fit two workgroups per CU).
+  constexpr int kPartBytes = 4 * TM * kPad * 4;
+  constexpr int kUnion = kPartBytes > 2 * kStageBytes ? kPartBytes : 2 * kStageBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kUnion];
+  char(*stage)[kStageBytes] = reinterpret_cast<char(*)[kStageBytes]>(smem);
+  float(*part)[TM][kPad] = reinterpret_cast<float(*)[TM][kPad]>(smem);
+  __shared__ float cand_v[3][KK][TM];
+  __shared__ float cand_s[3][KK][TM];
+  __shared__ int cand_i[3][KK][TM];
+  __shared__ int hist[kMaxExperts];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rc = wave & 3;
+  const int g = wave >> 2;
+  const int q = lane >> 4;
+  const int r16 = lane & 15;
+  const int t0 = blockIdx.x * TM;
+  const int steps = d / 32;
+  const int nch = ceil_div(steps, kStageSteps);
+
+  if (tid < kMaxExperts) hist[tid] = 0;
+  float bq[kSelQ];
+  load_selection_bias(bias, wave, E, bq);
+
+  // This thread's pieces of a chunk: row er (expert, clamped below E), piece
+  // c (16 B) of the row's 512 B; the last chunk's pieces past d are clamped
+  // to d's last piece (loaded, never used: their steps are skipped).
+  const bf16_t* wrow[kPieces];
+  int wcol[kPieces];  // the piece's first element within the chunk's 256
+  int wdst[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int slot = tid + i * kThreads;
+    const int er = slot / (kStageRowBytes / 16);
+    const int c = slot % (kStageRowBytes / 16);
+    wrow[i] = wr + (size_t)min(er, E - 1) * d;
+    wcol[i] = c * 8;
+    wdst[i] = er * kStageRowBytes + ((c ^ (er & 7)) << 4);
+  }
+  const bf16_t* xrow = x + (size_t)min(t0 + g * 16 + r16, T - 1) * d + q * 8;
+
+  u32x4 wq[kChunksAhead][kPieces];
+  u32x4 xq[kChunksAhead][2];
+  auto load_chunk = [&](int j, u32x4 (&w)[kPieces], u32x4 (&xf)[2]) {
+    const int jj = min(j, nch - 1);  // past the end: reload the last chunk (never used)
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      w[i] = load16(wrow[i] + min(jj * kStageSteps * 32 + wcol[i], d - 8));
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int st = min(jj * kStageSteps + 4 * u + rc, steps - 1);
+      xf[u] = load16(xrow + st * 32);
+    }
+  };
+#pragma unroll
+  for (int a = 0; a < kChunksAhead; ++a) load_chunk(a, wq[a], xq[a]);
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb) acc[eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int j0 = 0; j0 < nch; j0 += kChunksAhead) {
+#pragma unroll
+    for (int a = 0; a < kChunksAhead; ++a) {
+      const int j = j0 + a;
+      if (j < nch) {  // uniform
+        char* buf = stage[j & 1];
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) *reinterpret_cast<u32x4*>(buf + wdst[i]) = wq[a][i];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int st = j * kStageSteps + 4 * u + rc;
+          if (st < steps) {  // uniform per wave
+            Frag16 av;
+            av.u = xq[a][u];
+#pragma unroll
+            for (int eb = 0; eb < 4; ++eb) {
+              const int row = eb * 16 + r16;
+              const int c = (4 * u + rc) * 4 + q;
+              Frag16 bw;
+              bw.u = *reinterpret_cast<const u32x4*>(buf + row * kStageRowBytes + ((c ^ (row & 7)) << 4));
+              acc[eb] = mfma16x16x32(av.h, bw.h, acc[eb]);
+            }
+          }
+        }
+        load_chunk(j + kChunksAhead, wq[a], xq[a]);
+      }
+    }
+  }
+  __syncthreads();  // every wave is done reading the weight buffers
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[rc][g * 16 + q * 4 + i][eb * 16 + r16] = acc[eb][i];
+  __syncthreads();
+  select_lane_token<TM, KK>(part, cand_v, cand_s, cand_i, wave, lane, bq, E, k, scale, t0, T,
+                            idx_out, w_out, chunk_counts != nullptr ? hist : nullptr);
+  if (chunk_counts != nullptr) {
+    __syncthreads();
+    if (tid < E) chunk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
+  }
+}
+
+// Router kernel and tokens per workgroup for T.  The tile router's sizes were
+// measured on the value layer's shape with the benchmark's inputs (the token
+// rows are not cache-resident: a 32-token tile router is faster at T = 8192
+// only when they are).
+struct RouterChoice {
+  bool staged;  // router_staged_kernel, else router_tile_kernel
+  int tokens;   // tokens per workgroup (the dispatch chunk)
+};
+
+// Tile-router workgroup size by T (tokens re-read the weight from L2 per
+// workgroup: larger tiles once there are enough workgroups).
+static int tile_router_tokens(int T) { return T <= 8192 ? 16 : T <= 16384 ? 32 : 64; }
+
+// Measured with the value layer's shape (routing alone, graph replay):
+//   T       tile   staged 32 tokens
+//   4096    17.2   21.8 us
+//   8192    28.8   24.8
+//   16384   37.9   32.9
+//   32768   48.6   59.6
+// so the staged router takes the middle range.  MOVA_ROUTER=tile, staged32
+// or staged64 forces a kernel (measurement, tests).
+static RouterChoice router_choice(int T) {
+  const char* v = getenv("MOVA_ROUTER");
+  if (v != nullptr) {
+    if (strcmp(v, "tile") == 0) return {false, tile_router_tokens(T)};
+    if (strcmp(v, "staged32") == 0) return {true, 32};
+    if (strcmp(v, "staged64") == 0) return {true, 64};
+  }
+  if (T > 6144 && T <= 16384) return {true, 32};
+  return {false, tile_router_tokens(T)};
+}
+
+int router_tile_tokens(int T) { return router_choice(T).tokens; }
 
 hipError_t launch_router_tile(const RouterArgs& a, hipStream_t stream) {
-  const int TM = router_tile_tokens(a.T);
+  const RouterChoice rch = router_choice(a.T);
+  const int TM = rch.tokens;
   const dim3 grid(ceil_div(a.T, TM));
+  if (rch.staged) {
+    const bool small_k = a.k <= 4;
+#define MOVA_ROUTER_STAGED(TMV, KK)                                                      \
+  router_staged_kernel<TMV, KK><<<grid, 16 * TMV, 0, stream>>>(                          \
+      a.x, a.wr, a.bias, a.T, a.d, a.E, a.k, a.scale, a.idx, a.w, a.chunk_counts)
+    if (TM == 32) {
+      if (small_k) MOVA_ROUTER_STAGED(32, 4); else MOVA_ROUTER_STAGED(32, 8);
+    } else {
+      if (small_k) MOVA_ROUTER_STAGED(64, 4); else MOVA_ROUTER_STAGED(64, 8);
+    }
+#undef MOVA_ROUTER_STAGED
+    return hipGetLastError();
+  }
 #define MOVA_ROUTER_TILE(TG, U, KK)                                                            \
   router_tile_kernel<TG, U, KK><<<grid, 256, 0, stream>>>(a.x, a.wr, a.bias, a.T, a.d, a.E, a.k, \
                                                           a.scale, a.idx, a.w, a.chunk_counts)

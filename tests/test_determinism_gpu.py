@@ -147,3 +147,28 @@ def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode, monkeypat
         assert bool((dec[1][:, 0] == E // 2).all())
 
 
+
+
+@pytest.mark.parametrize("T,d,E,k", [(4096, 2560, 64, 4), (1000, 320, 40, 8), (777, 192, 7, 3),
+                                     (8192, 2560, 64, 4), (33, 2560, 64, 6)])
+def test_staged_router_bitwise(T, d, E, k, monkeypatch):
+    """The staged-weight router (32- or 64-token workgroups, the weight shared
+    through LDS) gives the tile router's routing bits, and the grouped path
+    built on its dispatch chunks gives the same output bits."""
+    shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=1, head_dim=64)
+    g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, T + d, torch.bfloat16, "uniform").items()}
+    monkeypatch.setenv("MOVA_PATH", "grouped")
+    res = {}
+    for kind in ("tile", "staged32", "staged64"):
+        monkeypatch.setenv("MOVA_ROUTER", kind)
+        print(f"router {kind} T={T} d={d} E={E} k={k}", flush=True)
+        idx, w = binding.route(g["x"], g["router_w"], g["router_b"], k, 2.5)
+        out = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, 2.5,
+                                    1, 64)
+        torch.cuda.synchronize()
+        res[kind] = (idx, w, out)
+    monkeypatch.delenv("MOVA_ROUTER", raising=False)
+    monkeypatch.delenv("MOVA_PATH")
+    for kind in ("staged32", "staged64"):
+        for name, a, b in zip(("idx", "w", "out"), res[kind], res["tile"]):
+            assert torch.equal(a, b), f"{kind}: {name} differs from the tile router"
