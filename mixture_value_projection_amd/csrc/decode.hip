@@ -24,16 +24,18 @@
 // trip, and keeps the weights in LDS for the epilogue.  Tokens are handled 16
 // at a time (one MFMA row group), or 32 at a time (two row groups) when the
 // expert has more than 16; an expert with more than 32 tokens takes several
-// passes over its weights.  The epilogue writes w * SiLU(z) (fp16,
-// rounded once) to the pair's partial row, like the grouped GEMM; the combine
-// kernel then sums each token's k partials in slot order.  The MFMA chain of
-// every (token, column) runs over the k steps in order, as in the grouped
-// GEMM, so both paths give identical bits.  (A fused last-arriver combine was measured and rejected:
-// the agent-scope release each workgroup needs costs far more than the
-// separate combine launch.)
+// passes over its weights.  For the value experts the epilogue writes
+// w * SiLU(z) (fp16, rounded once) to the pair's partial row, like the grouped
+// GEMM; the combine kernel then sums each token's k partials in slot order.
+// The MFMA chain of every (token, column) runs over the k steps in order, as
+// in the grouped GEMM, so both paths give identical bits.  (A fused
+// last-arriver combine was measured and rejected: the agent-scope release
+// each workgroup needs costs far more than the separate combine launch.)
 //
 // 64 experts x 1024 columns is 512 workgroups of 4 waves: at two workgroups
 // per CU (up to 256 registers per lane) the whole grid is resident at once.
+// The FFN's projections (100 experts, 1536 or 2560 columns) run in a few
+// rounds of workgroups.
 #include <type_traits>
 
 #include "common.h"
