@@ -240,7 +240,11 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
  * and the shared expert's output are kept as fp16; the sum is fp32 in slot
  * order, the shared term last, rounded once to bf16.  Logits for the top-k
  * are fp32: four MFMA chains per (token, expert) over the k steps of each
- * residue class mod 4, in order, added in class order.  Errors as for
+ * residue class mod 4, in order, added in class order.  Results are bitwise
+ * reproducible for identical inputs.  A token's row does not depend on the
+ * other tokens of the call, except that the shared expert runs a split-k
+ * kernel up to T = 256 and the tiled GEMM above, which sum in different
+ * orders (rows agree to rounding across that boundary).  Errors as for
  * mova_value_forward.
  * Streams: the shared expert depends on x alone and runs on a stream the
  * library owns for the current device (created on first use, default
