@@ -128,6 +128,50 @@ def run_single_layer(name, steps, warmup, copies):
                 max_abs_out=max_abs_out)
 
 
+def run_tp_shard(name, tp, steps, warmup):
+    """One GPU's share of a workload under tensor parallelism over the KV
+    heads: the router replicated, every expert's rows for heads [0, 8 / tp)
+    (N = 1024 / tp), the workload's real T.  Weight copies are rotated so that
+    together they exceed twice the 256 MB Infinity Cache."""
+    w = inputs.WORKLOADS[name]
+    sh = w.shape
+    heads = sh.n_kv_heads // tp
+    N = heads * sh.head_dim
+    x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
+    full = inputs.make_weights(sh, w.seed, w.dtype, w.bias)
+    base = {"router_w": full["router_w"].to(DEV), "router_b": full["router_b"].to(DEV),
+            "expert_w": full["expert_w"][:, :N, :].contiguous().to(DEV)}
+    del full
+    shard_bytes = base["expert_w"].numel() * 2
+    copies = max(4, -(-2 * 256 * 2**20 // shard_bytes))
+    cps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(copies - 1)]
+    out = torch.empty(sh.T, heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty(sh.T, sh.k, dtype=torch.int32, device=DEV)
+    ws = torch.empty(binding.workspace_bytes(sh.T, sh.d, sh.E, sh.k, heads, sh.head_dim),
+                     dtype=torch.uint8, device=DEV)
+    binding.value_forward(x, base["router_w"], base["router_b"], base["expert_w"], sh.k, sh.scale,
+                          heads, sh.head_dim, out=out, topk_idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    touched = int((np.bincount(idx.cpu().numpy().ravel(), minlength=sh.E) > 0).sum())
+    calls = [(lambda c=c: binding.value_forward(x, c["router_w"], c["router_b"], c["expert_w"],
+                                                sh.k, sh.scale, heads, sh.head_dim, out=out,
+                                                workspace=ws)) for c in cps]
+    gsecs, gcalls = graph_time(calls, steps, warmup)
+    us = 1e6 * gsecs / gcalls
+    del cps, calls
+    d = {"tp": tp, "workload": name, "T": sh.T, "n_kv_heads": heads, "N": N, "weight_copies": copies,
+         "us_per_call": us, "tokens_per_s": sh.T / (us * 1e-6)}
+    if name == "decode":
+        nbytes = touched * N * sh.d * 2 + sh.T * sh.d * 2
+        d["GB_per_s"] = nbytes / (us * 1e-6) / 1e9
+        d["frac_hbm"] = nbytes / (us * 1e-6) / accounting.HBM_PEAK_BPS
+    else:
+        flops = 2.0 * sh.T * (sh.k * sh.d * N + sh.d * sh.E)
+        d["tflops"] = flops / (us * 1e-6) / 1e12
+        d["frac_bf16_peak"] = flops / (us * 1e-6) / accounting.BF16_MFMA_PEAK_FLOPS
+    return d
+
+
 def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
     """The decode step with its value rows stored straight into a paged pool
     (num_blocks x block_size slots of [8, 128] bf16, 128 MB) at distinct
@@ -495,6 +539,16 @@ def main():
                                 "tokens_per_s": sh.T / (pus * 1e-6),
                                 "pool": "4096 blocks x 16 slots x [8, 128] bf16, distinct random "
                                         "slots, no contiguous output"}
+        torch.cuda.empty_cache()
+        log("tensor-parallel shards ...")
+        shards = []
+        for tp in (2, 8):
+            shards.append(run_tp_shard("decode", tp, args.steps, args.warmup))
+            torch.cuda.empty_cache()
+            shards.append(run_tp_shard("prefill", tp, max(5, args.steps // 10),
+                                       max(2, args.warmup // 4)))
+            torch.cuda.empty_cache()
+        line["tp_shard"] = shards
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline()

@@ -36,6 +36,9 @@
 // per CU (up to 256 registers per lane) the whole grid is resident at once.
 // The FFN's projections (100 experts, 1536 or 2560 columns) run in a few
 // rounds of workgroups.
+#include <stdlib.h>
+#include <string.h>
+
 #include <type_traits>
 
 #include "common.h"
@@ -43,8 +46,8 @@
 
 namespace mova {
 
-constexpr int kSlice = 128;   // columns per workgroup (32 per wave)
-constexpr int kGroups = 2;    // 16-column MFMA groups per wave
+// kGroups: 16-column MFMA groups per wave (2, or 1 for narrow outputs, see
+// launch_decode_mode); a workgroup's 4 waves cover 64 * kGroups columns.
 
 // kUnroll: k steps per batch; it divides the step count d / 32 (4 when it
 // can, else 2, which always does since d % 64 == 0).  kPair32: experts with
@@ -59,7 +62,7 @@ constexpr int kGroups = 2;    // 16-column MFMA groups per wave
 //                      up block, and c = its first column / 2 + lane % 16)
 //   kGemmRoutedLinear  partial[pair, n] = fp16(w * z), A rows one per pair
 //                      (FFN down, A = the pairs' h rows)
-template <int kUnroll, bool kPair32, int kMode>
+template <int kUnroll, bool kPair32, int kMode, int kGroups>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
@@ -70,6 +73,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ float wlist[kDecodeMaxT * kMaxTopK];
   __shared__ int wave_hits[4];
 
+  static_assert(kGroups == 2 || (kGroups == 1 && kMode != kGemmRoutedSwiGLU),
+                "SwiGLU pairs a gate group with its up group in one wave");
+  constexpr int kSlice = 64 * kGroups;
   const int slices = ceil_div(N, kSlice);
   const int e = blockIdx.x / slices;
   const int n0 = (blockIdx.x % slices) * kSlice;
@@ -85,7 +91,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const bf16_t* wrow[kGroups];
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
-    ncol[g] = n0 + wave * 32 + g * 16 + r16;
+    ncol[g] = n0 + wave * 16 * kGroups + g * 16 + r16;
     wrow[g] = W + ((size_t)e * N + min(ncol[g], N - 1)) * d + q * 8;
   }
   const int nb = d / 32 / kUnroll;  // exact by the choice of kUnroll
@@ -217,13 +223,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+template <int kMode, int kGroups>
+static auto pick_decode_kernel(bool unroll4, bool pair32) {
+  return unroll4 ? (pair32 ? decode_kernel<4, true, kMode, kGroups>
+                           : decode_kernel<4, false, kMode, kGroups>)
+                 : (pair32 ? decode_kernel<2, true, kMode, kGroups>
+                           : decode_kernel<2, false, kMode, kGroups>);
+}
+
+// Narrow outputs (e.g. one GPU's share of the heads under tensor parallelism)
+// give too few 128-column workgroups to fill the GPU's two per CU: one
+// 16-column group per wave then doubles the workgroups (and the MFMA chains
+// running at once).  Each group's chain is the same either way, so are the
+// bits.  The SwiGLU epilogue needs a gate and an up group in one wave.
 template <int kMode>
 static hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.E * ceil_div(a.N, kSlice));
+  constexpr int kRound = 512;  // two workgroups per CU
+  bool narrow = (long long)a.E * ceil_div(a.N, 128) < kRound;
+  const char* force = getenv("MOVA_DECODE_GROUPS");  // 1 or 2 (tests, measurement)
+  if (force != nullptr && (strcmp(force, "1") == 0 || strcmp(force, "2") == 0))
+    narrow = force[0] == '1';
+  narrow = narrow && kMode != kGemmRoutedSwiGLU;
+  const dim3 grid(a.E * ceil_div(a.N, narrow ? 64 : 128));
   const bool unroll4 = (a.d / 32) % 4 == 0;
   const bool pair32 = a.T > 64;
-  auto kern = unroll4 ? (pair32 ? decode_kernel<4, true, kMode> : decode_kernel<4, false, kMode>)
-                      : (pair32 ? decode_kernel<2, true, kMode> : decode_kernel<2, false, kMode>);
+  auto kern = narrow ? pick_decode_kernel<kMode, kMode == kGemmRoutedSwiGLU ? 2 : 1>(unroll4, pair32)
+                     : pick_decode_kernel<kMode, 2>(unroll4, pair32);
   kern<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, (bf16_t*)a.out_h, a.T, a.d,
                                  a.N, a.E, a.k);
   return hipGetLastError();

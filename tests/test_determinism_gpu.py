@@ -172,3 +172,22 @@ def test_staged_router_bitwise(T, d, E, k, monkeypatch):
     for kind in ("staged32", "staged64"):
         for name, a, b in zip(("idx", "w", "out"), res[kind], res["tile"]):
             assert torch.equal(a, b), f"{kind}: {name} differs from the tile router"
+
+
+@pytest.mark.parametrize("groups", ["1", "2"])
+@pytest.mark.parametrize("T,d,E,k,heads,hd", [(64, 2560, 64, 4, 1, 128), (64, 2560, 64, 4, 4, 128),
+                                              (100, 512, 16, 3, 3, 64), (256, 256, 40, 8, 1, 64),
+                                              (7, 320, 5, 2, 2, 32)])
+def test_decode_column_groups_bitwise(groups, T, d, E, k, heads, hd, monkeypatch):
+    """The decode kernel with one or two 16-column groups per wave (narrow
+    outputs, e.g. one GPU's share of the heads, take one) gives the grouped
+    path's bits."""
+    shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=heads, head_dim=hd)
+    g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, T + E + heads, torch.bfloat16, "uniform").items()}
+    print(f"decode groups={groups} T={T} d={d} E={E} k={k} N={heads * hd}", flush=True)
+    monkeypatch.setenv("MOVA_DECODE_GROUPS", groups)
+    dec = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
+    monkeypatch.delenv("MOVA_DECODE_GROUPS")
+    grp = _run(g, k, heads, hd, {"MOVA_PATH": "grouped"}, monkeypatch)
+    for name, a, b in zip(("out", "idx", "w"), dec, grp):
+        assert torch.equal(a, b), f"{name}: decode ({groups} groups) differs from the grouped path"
