@@ -29,9 +29,9 @@
 // consecutive 16-byte slots, the swizzle is applied when choosing which
 // global chunk each lane loads.
 //
-// Tile choice (measured on the decode, prefill, chunked and skewed shapes):
-// grouped mode takes 128 x 128 (2 stages, two workgroups per CU) while the
-// experts average at most 384 rows, else 256 x 256; dense mode takes 256 x
+// Tile choice (measured): grouped mode takes 128 x 128 (2 stages, two
+// workgroups per CU) or 256 x 256 by the experts' average row count
+// (gemm_tile_grouped); dense mode takes 256 x
 // 256 once those tiles fill the 256 CUs, else 128 x 128 with 4 stages when
 // the grid is a single round of workgroups and 2 stages otherwise.
 //
@@ -112,9 +112,26 @@ static bool forced_tile(GemmTile* t) {
 GemmTile gemm_tile_grouped(int T, int k, int E) {
   GemmTile t;
   if (forced_tile(&t)) return t;
-  // 128 x 128 tiles (two workgroups per CU) while the experts average at most
-  // 384 rows (one and a half 256-row tiles), where 256-row tiles carry much
-  // padding; 256 x 256 above.
+  // By the experts' average row count R = T k / E.  Which tile wins depends
+  // on how each rounds the experts' rows up to whole M-tiles and the tiles up
+  // to whole rounds of workgroups (two 128 x 128 or one 256 x 256 per CU), so
+  // it alternates; measured on the value layer (d = 2560, N = 1024, E = 64,
+  // seeded uniform routing), call times in us:
+  //   R        48   96   128  192  224  256  288  320  384  448  512
+  //   128x128  100  115  150  154  188  196  207  235  247  281  300
+  //   256x256  114  119  124  137  201  197  209  212  218  285  289
+  // 128 x 128 up to R = 112 and from 209 to 304, 256 x 256 elsewhere.
+  const long long R = ((long long)T * k + E / 2) / E;
+  if (R <= 112 || (R > 208 && R <= 304)) return {128, 128, 8, 2};
+  return {256, 256, 8, 2};
+}
+
+GemmTile gemm_tile_grouped_ffn(int T, int k, int E) {
+  GemmTile t;
+  if (forced_tile(&t)) return t;
+  // The FFN's experts (E = 100, 1536 / 2560 columns): 128 x 128 while they
+  // average at most 384 rows (measured at T = 4096, 328 rows: faster than or
+  // level with 256 x 256), 256 x 256 above.
   if ((long long)T * k <= 384ll * E) return {128, 128, 8, 2};
   return {256, 256, 8, 2};
 }

@@ -613,7 +613,7 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
   const bool decode = choose_ffn_path(T, k) == Path::Decode;
-  const GemmTile tile = gemm_tile_grouped(T, k, E);
+  const GemmTile tile = gemm_tile_grouped_ffn(T, k, E);
   if (!decode) {
     StageScope sc(1, stream);
     DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, ffn_router_chunk_tokens(), tile.bm};
