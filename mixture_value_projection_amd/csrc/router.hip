@@ -488,12 +488,10 @@ struct RouterChoice {
 static int tile_router_tokens(int T) { return T <= 8192 ? 16 : T <= 16384 ? 32 : 64; }
 
 // Measured with the value layer's shape (routing alone, graph replay):
-//   T       tile   staged 32 tokens
-//   4096    17.2   21.8 us
-//   8192    28.8   24.8
-//   16384   37.9   32.9
-//   32768   48.6   59.6
-// so the staged router takes the middle range.  MOVA_ROUTER=tile, staged32
+//   T       4096  4608  6144  8192  16384  20480  28672  32768
+//   tile    17.2  28.4  28.9  28.8  38.4   47.9   48.8   48.6 us
+//   staged  21.8  22.6  24.3  24.8  33.1   49.4   58.2   59.6   (32 tokens)
+// so the staged router takes 4096 < T <= 18432.  MOVA_ROUTER=tile, staged32
 // or staged64 forces a kernel (measurement, tests).
 static RouterChoice router_choice(int T) {
   const char* v = getenv("MOVA_ROUTER");
@@ -502,7 +500,7 @@ static RouterChoice router_choice(int T) {
     if (strcmp(v, "staged32") == 0) return {true, 32};
     if (strcmp(v, "staged64") == 0) return {true, 64};
   }
-  if (T > 6144 && T <= 16384) return {true, 32};
+  if (T > 4096 && T <= 18432) return {true, 32};
   return {false, tile_router_tokens(T)};
 }
 
