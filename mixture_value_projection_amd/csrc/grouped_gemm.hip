@@ -129,10 +129,14 @@ GemmTile gemm_tile_grouped(int T, int k, int E) {
 GemmTile gemm_tile_grouped_ffn(int T, int k, int E) {
   GemmTile t;
   if (forced_tile(&t)) return t;
-  // The FFN's experts (E = 100, 1536 / 2560 columns): 128 x 128 while they
-  // average at most 384 rows (measured at T = 4096, 328 rows: faster than or
-  // level with 256 x 256), 256 x 256 above.
-  if ((long long)T * k <= 384ll * E) return {128, 128, 8, 2};
+  // The FFN's experts (E = 100, k = 8, 1536 / 2560 columns), the same kind
+  // of alternation as above; call times in us:
+  //   R        20   82   123  164  246  328  492   655
+  //   128x128  312  369  438  507  602  713  981   1225
+  //   256x256  372  419  451  478  605  724  888   1130
+  // 128 x 128 up to R = 144 and from 209 to 384, 256 x 256 elsewhere.
+  const long long R = ((long long)T * k + E / 2) / E;
+  if (R <= 144 || (R > 208 && R <= 384)) return {128, 128, 8, 2};
   return {256, 256, 8, 2};
 }
 
