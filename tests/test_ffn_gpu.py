@@ -80,6 +80,7 @@ CASES = [
                                    # one expert, and 2.5 would push |out| past the range
                                    # the max-abs rule is set for)
     (257, 256, 100, 8, 64, 192),
+    (2048, 2560, 100, 8, 768, 768),  # 256 x 256 tiles (the experts average 164 rows)
     (4096, 2560, 100, 8, 768, 768),
 ]
 
@@ -233,3 +234,32 @@ def test_ffn_concurrent_host_threads():
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
     assert not errors, errors
+
+
+FFN_TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4"]
+
+
+@pytest.mark.parametrize("T,d,E,k,inter,inter_s", [(300, 512, 12, 4, 128, 64), (700, 320, 20, 8, 64, 0)])
+def test_ffn_every_tile_shape(T, d, E, k, inter, inter_s, monkeypatch):
+    """The FFN's grouped GEMMs (SwiGLU gate/up, weighted down) in every tile
+    shape: each against the oracle, and all of them with the same bits."""
+    sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s)
+    L, g = gpu_layer(sh, seed=T + E)
+    o = {kk: v.double().numpy() for kk, v in L.items()}
+    ref = oracle.route(o["x"], o["router_w"], o["router_b"], k, sh.scale)
+    monkeypatch.setenv("MOVA_PATH", "grouped")
+    outs = {}
+    for tile in FFN_TILES:
+        monkeypatch.setenv("MOVA_GEMM_TILE", tile)
+        say(f"ffn tile {tile}: T={T} d={d} E={E} k={k} inter={inter} shared={inter_s}")
+        out, idx, w = run_ffn(g, sh)
+        if tile == FFN_TILES[0]:
+            rc = P.check_routing(idx, w, ref, sh.scale)
+            rows = np.arange(T)
+            want = ffn_reference(L, sh, rows, rc.effective_idx, rc.effective_w)
+            say(f"  {P.check_output(out, want, what=f'ffn tile {tile}')}")
+        outs[tile] = out
+    monkeypatch.delenv("MOVA_GEMM_TILE")
+    monkeypatch.delenv("MOVA_PATH")
+    for tile, out in outs.items():
+        assert torch.equal(out, outs[FFN_TILES[0]]), f"{tile} differs from {FFN_TILES[0]}"
