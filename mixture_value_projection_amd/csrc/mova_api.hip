@@ -73,14 +73,17 @@ Path choose_ffn_path(int T, int k) {
 //   idx [T*k] i32 | w [T*k] f32 | chunk_counts [C*E] i32 | expert_off [E+1] i32 |
 //   tile_base [E+1] i32 | plog (small-T router partial logits, T <= kDecodeMaxT
 //   only) | perm [T*k] i32 | partial [T*k*N] f16
-// C = number of tile-router workgroups (dispatch chunks).
+// C = dispatch chunks at the smallest router workgroup (16 tokens), so that
+// the size depends on the shapes alone, whichever router kernel runs.
 struct Layout {
   size_t idx, w, chunk, eoff, tbase, plog, perm, partial, total;
 };
 
+constexpr int kMinRouterChunk = 16;
+
 Layout layout(int T, int E, int k, int N) {
   const size_t pairs = (size_t)T * k;
-  const size_t C = (size_t)ceil_div(T, router_tile_tokens(T));
+  const size_t C = (size_t)ceil_div(T, kMinRouterChunk);
   Layout L;
   size_t o = 0;
   L.idx = o;     o += align256(pairs * 4);

@@ -504,7 +504,7 @@ static RouterChoice router_choice(int T) {
   return {false, tile_router_tokens(T)};
 }
 
-int router_tile_tokens(int T) { return router_choice(T).tokens; }
+int router_tile_tokens(int T) { return router_choice(T).tokens; }  // >= 16 for every choice
 
 hipError_t launch_router_tile(const RouterArgs& a, hipStream_t stream) {
   const RouterChoice rch = router_choice(a.T);

@@ -70,6 +70,19 @@ def test_workspace_bytes(lib):
     assert lib.mova_workspace_bytes(-1, 2560, 64, 4, 8, 128) == bad
 
 
+@pytest.mark.parametrize("T", [100, 4096, 5000, 8192, 20000, 40000])
+def test_workspace_bytes_independent_of_kernel_choice(T, monkeypatch):
+    """The workspace size depends on the shapes alone, not on which router or
+    expert kernel a call will take (the switches that force them)."""
+    want = binding.workspace_bytes(T, 2560, 64, 4, 8, 128)
+    for var, val in [("MOVA_ROUTER", "tile"), ("MOVA_ROUTER", "staged32"),
+                     ("MOVA_ROUTER", "staged64"), ("MOVA_PATH", "grouped"),
+                     ("MOVA_PATH", "decode"), ("MOVA_GEMM_TILE", "128x128")]:
+        monkeypatch.setenv(var, val)
+        assert binding.workspace_bytes(T, 2560, 64, 4, 8, 128) == want, (var, val)
+        monkeypatch.delenv(var)
+
+
 def fwd(lib, **kw):
     a = dict(x=FAKE, rw=FAKE, rb=None, ew=FAKE, T=16, d=256, E=8, k=2, scale=2.5, H=2, D=32,
              out=FAKE, idx=None, w=None, ws=FAKE, wsb=1 << 30, stream=None)
