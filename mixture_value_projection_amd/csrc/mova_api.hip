@@ -347,8 +347,9 @@ int mova_route(const void* x, const void* router_w, const float* router_b, int T
     return MOVA_ERR_INVALID_ARG;
   RouterArgs ra{(const __bf16*)x, (const __bf16*)router_w, router_b, T, d, E, k, scale,
                 topk_idx, topk_w, nullptr};
-  // Routing alone has no workspace, so it uses the single-kernel tile router
-  // (same bits as the two-kernel small-T router of the decode path).
+  // Routing alone has no workspace, so it uses the single-kernel routers
+  // (tile or staged by T; same bits as the two-kernel small-T router of the
+  // decode path).
   return launch_router_tile(ra, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }
 
