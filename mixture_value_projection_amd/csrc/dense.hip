@@ -197,16 +197,17 @@ hipError_t launch_dense_skinny(const DenseArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(S * (a.N / 16)));
   auto kern = rgt >= 3 ? dense_skinny_kernel<4>
                        : (rgt == 2 ? dense_skinny_kernel<2> : dense_skinny_kernel<1>);
-  static bool attr_set = false;
-  if (!attr_set) {
+  static std::atomic<unsigned long long> attr_done{0};
+  hipError_t aerr = once_per_device(attr_done, []() {
     const int max_lds = kSkinnyWaves * kDenseSkinnyMaxT * 16 * (int)sizeof(float);
     for (auto k : {dense_skinny_kernel<1>, dense_skinny_kernel<2>, dense_skinny_kernel<4>}) {
       hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize,
                                          max_lds);
       if (e != hipSuccess) return e;
     }
-    attr_set = true;
-  }
+    return hipSuccess;
+  });
+  if (aerr != hipSuccess) return aerr;
   kern<<<grid, 256, lds, stream>>>(a.x, a.W, a.part, a.T, a.d, a.N);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

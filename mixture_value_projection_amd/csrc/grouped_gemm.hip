@@ -407,13 +407,11 @@ hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) 
   auto kern = gemm_kernel<MOVA_TILE_ARGS, kMode>;
   constexpr int smem = kS * Tile<MOVA_TILE_ARGS>::kStage;
   constexpr int threads = Tile<MOVA_TILE_ARGS>::kThreads;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  static std::atomic<unsigned long long> attr_done{0};
+  hipError_t err = once_per_device(attr_done, [&]() {
+    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  });
+  if (err != hipSuccess) return err;
   const long long grid = ((tiles + kXcds - 1) / kXcds) * kXcds;
   kern<<<dim3((unsigned)grid), threads, smem, stream>>>(a.x, a.W, a.perm, a.topk_w, a.expert_off,
                                                          a.tile_base, a.partial, a.out, a.T, a.d,

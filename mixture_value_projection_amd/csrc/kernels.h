@@ -1,12 +1,29 @@
 // Internal launch interface between the C ABI (mova_api.hip) and the kernels.
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "common.h"
 
 namespace mova {
+
+// Runs set() once per device, for per-device function attributes (device
+// ordinals from 64 on: every call).  Thread-safe: concurrent first calls may
+// both run set(), which must be idempotent.
+template <class F>
+inline hipError_t once_per_device(std::atomic<unsigned long long>& done, F set) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = (dev >= 0 && dev < 64) ? 1ull << dev : 0ull;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = set();
+  if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 struct RouterArgs {
   const __bf16* x;
