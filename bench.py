@@ -172,6 +172,48 @@ def run_tp_shard(name, tp, steps, warmup):
     return d
 
 
+def run_ep_shard(name, ep, steps, warmup):
+    """One GPU's share of a workload under expert parallelism: experts
+    [0, E / ep) with the routing the replicated router chose, every slot on
+    another GPU's expert marked unused (-1).  mova_value_from_routing then
+    runs only this GPU's pairs and writes its partial sums [T, N], the input
+    of the reduce-scatter that would combine the GPUs' shares."""
+    w = inputs.WORKLOADS[name]
+    sh = w.shape
+    e_local = sh.E // ep
+    x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
+    full = inputs.make_weights(sh, w.seed, w.dtype, w.bias)
+    rw, rb = full["router_w"].to(DEV), full["router_b"].to(DEV)
+    base = full["expert_w"][:e_local].contiguous().to(DEV)
+    del full
+    shard_bytes = base.numel() * 2
+    copies = max(4, -(-2 * 256 * 2**20 // shard_bytes))
+    cps = [base] + [base.clone() for _ in range(copies - 1)]
+    idx, wts = binding.route(x, rw, rb, sh.k, sh.scale)
+    local = torch.where(idx < e_local, idx, torch.full_like(idx, -1)).contiguous()
+    pairs = int((local >= 0).sum())
+    touched = int(torch.unique(local[local >= 0]).numel())
+    out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(binding.workspace_bytes(sh.T, sh.d, e_local, sh.k, sh.n_kv_heads, sh.head_dim),
+                     dtype=torch.uint8, device=DEV)
+    calls = [(lambda c=c: binding.value_from_routing(x, local, wts, c, sh.n_kv_heads, sh.head_dim,
+                                                     out=out, workspace=ws)) for c in cps]
+    gsecs, gcalls = graph_time(calls, steps, warmup)
+    us = 1e6 * gsecs / gcalls
+    del cps, calls
+    d = {"ep": ep, "workload": name, "T": sh.T, "experts": e_local, "local_pairs": pairs,
+         "weight_copies": copies, "us_per_call": us}
+    if name == "decode":
+        nbytes = touched * sh.N * sh.d * 2 + sh.T * sh.d * 2
+        d["GB_per_s"] = nbytes / (us * 1e-6) / 1e9
+        d["frac_hbm"] = nbytes / (us * 1e-6) / accounting.HBM_PEAK_BPS
+    else:
+        flops = 2.0 * pairs * sh.d * sh.N
+        d["tflops"] = flops / (us * 1e-6) / 1e12
+        d["frac_bf16_peak"] = flops / (us * 1e-6) / accounting.BF16_MFMA_PEAK_FLOPS
+    return d
+
+
 def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
     """The decode step with its value rows stored straight into a paged pool
     (num_blocks x block_size slots of [8, 128] bf16, 128 MB) at distinct
@@ -549,6 +591,15 @@ def main():
                                        max(2, args.warmup // 4)))
             torch.cuda.empty_cache()
         line["tp_shard"] = shards
+        log("expert-parallel shards ...")
+        shards = []
+        for ep in (2, 8):
+            shards.append(run_ep_shard("decode", ep, args.steps, args.warmup))
+            torch.cuda.empty_cache()
+            shards.append(run_ep_shard("prefill", ep, max(5, args.steps // 10),
+                                       max(2, args.warmup // 4)))
+            torch.cuda.empty_cache()
+        line["ep_shard"] = shards
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline()
