@@ -39,6 +39,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -223,6 +224,125 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---- very small T: each chain's weights in registers, k split over waves ----
+//
+// With a handful of tokens only a few experts are touched, so the kernel
+// above runs few workgroups, each walking its k loop in several rounds of
+// loads.  Here a workgroup owns one (touched expert, 16-column group), 80 KB
+// of weights at d = 2560: its 4 waves each load one quarter of the group's k
+// steps (weight and token fragments) into registers at once, and the MFMA
+// chain of the 16 x 16 output tile then runs through the quarters in order,
+// wave after wave, the fp32 accumulator handed on through LDS.  It is the
+// same chain as in the other kernels (same operands, same order), so the
+// bits are the same.  Workgroup i takes the (i / groups)-th touched expert in
+// index order (the touched set is read from the routing); the weights stay in
+// registers across passes of 16 pairs.  Value experts only (w * SiLU(z)).
+constexpr int kChainMaxPairs = 64;  // T * k this kernel accepts
+constexpr int kChainAutoPairs = 32;  // T * k up to which it is the default
+
+template <int kQ>  // k steps per wave (at most)
+__global__ __launch_bounds__(256) void decode_chain_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
+    const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
+    f16_t* __restrict__ partial, int T, int d, int N, int E, int k) {
+  __shared__ int plist[kChainMaxPairs];
+  __shared__ float wlist[kChainMaxPairs];
+  __shared__ f32x4 handoff[64];
+  __shared__ unsigned long long touched;
+  __shared__ int wave_hits[4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int npairs = T * k;  // <= kChainMaxPairs (launch condition)
+  const int groups = N / 16;
+  const int rank = blockIdx.x / groups;
+  const int n0 = (blockIdx.x % groups) * 16;
+
+  // The routing, read once: the touched experts (E <= 64), this workgroup's
+  // one, and its pairs in pair order (one ballot round: npairs <= 64).
+  const bool in = tid < npairs;
+  const int pe = in ? idx[tid] : -1;
+  const float pwv = in ? topk_w[tid] : 0.f;
+  if (tid == 0) touched = 0ull;
+  __syncthreads();
+  if (pe >= 0 && pe < E) atomicOr(&touched, 1ull << pe);
+  __syncthreads();
+  uint64_t mask = touched;
+  if (rank >= __popcll(mask)) return;  // uniform across the workgroup
+  for (int i = 0; i < rank; ++i) mask &= mask - 1;
+  const int e = __ffsll((unsigned long long)mask) - 1;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const bool hit = pe == e;
+  const uint64_t mm = __ballot(hit);
+  if (lane == 0) wave_hits[wave] = __popcll(mm);
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_hits[w];
+  if (hit) {
+    const int slot = before + __popcll(mm & lt_mask);
+    plist[slot] = tid;
+    wlist[slot] = pwv;
+  }
+  const int ce = (wave_hits[0] + wave_hits[1]) + (wave_hits[2] + wave_hits[3]);
+  __syncthreads();
+
+  // This wave's steps [s0, s0 + ns) of the chain.  Its weight fragments are
+  // requested together with the first pass's token fragments (one round trip).
+  const int steps = d / 32;
+  const int per = ceil_div(steps, 4);  // <= kQ (launch condition)
+  const int s0 = min(steps, wave * per);
+  const int ns = min(steps, s0 + per) - s0;
+  const bf16_t* wrow = W + ((size_t)e * N + n0 + r16) * d + q * 8;
+  Frag16 wf[kQ];
+#pragma unroll
+  for (int i = 0; i < kQ; ++i)
+    if (i < ns) wf[i].u = load16(wrow + (s0 + i) * 32);
+
+  for (int p0 = 0; p0 < ce; p0 += 16) {
+    // Token fragments of this pass (MFMA row r16 = pair p0 + r16; rows past
+    // the expert's pairs repeat its last pair and are never stored).
+    const bf16_t* xr = x + (size_t)(plist[min(p0 + r16, ce - 1)] / k) * d + q * 8;
+    Frag16 xf[kQ];
+#pragma unroll
+    for (int i = 0; i < kQ; ++i)
+      if (i < ns) xf[i].u = load16(xr + (s0 + i) * 32);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < 4; ++w) {
+      if (wave == w) {
+        if (w > 0) acc = handoff[lane];
+#pragma unroll
+        for (int i = 0; i < kQ; ++i)
+          if (i < ns) acc = mfma16x16x32(xf[i].h, wf[i].h, acc);
+        if (w < 3) handoff[lane] = acc;
+      }
+      __syncthreads();
+    }
+    if (wave == 3) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = p0 + q * 4 + v;
+        if (r < ce)
+          partial[(size_t)plist[r] * N + n0 + r16] = (f16_t)(wlist[r] * siluf(acc[v]));
+      }
+    }
+  }
+}
+
+// Whether the chain kernel takes a call, and with how many steps per wave.
+static int chain_steps_per_wave(const DecodeArgs& a) {
+  const char* v = getenv("MOVA_DECODE_CHAIN");  // 0 / 1 force it off / on (tests, measurement)
+  const bool force_off = v != nullptr && strcmp(v, "0") == 0;
+  const bool force_on = v != nullptr && strcmp(v, "1") == 0;
+  const int per = ceil_div(a.d / 32, 4);
+  const bool fits = a.mode == kGemmRoutedSilu && (long long)a.T * a.k <= kChainMaxPairs &&
+                    a.E <= 64 && a.N % 16 == 0 && per <= 24;
+  if (!fits || force_off) return 0;
+  if (!force_on && (long long)a.T * a.k > kChainAutoPairs) return 0;
+  return per <= 8 ? 8 : per <= 16 ? 16 : 24;
+}
+
 template <int kMode, int kGroups>
 static auto pick_decode_kernel(bool unroll4, bool pair32) {
   return unroll4 ? (pair32 ? decode_kernel<4, true, kMode, kGroups>
@@ -257,6 +377,13 @@ static hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.T > kDecodeMaxT || a.k > kMaxTopK || a.d % 64 != 0 || a.N % 64 != 0)
     return hipErrorInvalidValue;
+  if (const int q = chain_steps_per_wave(a)) {
+    const dim3 grid((unsigned)(std::min(a.E, a.T * a.k) * (a.N / 16)));
+    auto kern = q == 8 ? decode_chain_kernel<8> : q == 16 ? decode_chain_kernel<16>
+                                                          : decode_chain_kernel<24>;
+    kern<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N, a.E, a.k);
+    return hipGetLastError();
+  }
   switch (a.mode) {
     case kGemmRoutedSilu: return launch_decode_mode<kGemmRoutedSilu>(a, stream);
     case kGemmRoutedSwiGLU:

@@ -191,3 +191,24 @@ def test_decode_column_groups_bitwise(groups, T, d, E, k, heads, hd, monkeypatch
     grp = _run(g, k, heads, hd, {"MOVA_PATH": "grouped"}, monkeypatch)
     for name, a, b in zip(("out", "idx", "w"), dec, grp):
         assert torch.equal(a, b), f"{name}: decode ({groups} groups) differs from the grouped path"
+
+
+@pytest.mark.parametrize("T,d,E,k,heads,hd", [(1, 2560, 64, 4, 8, 128), (3, 2560, 64, 4, 8, 128),
+                                              (8, 2560, 64, 8, 8, 128), (16, 3072, 64, 4, 2, 128),
+                                              (5, 64, 7, 3, 1, 64), (2, 256, 64, 1, 1, 128),
+                                              (16, 512, 40, 4, 4, 64)])
+def test_decode_chain_kernel_bitwise(T, d, E, k, heads, hd, monkeypatch):
+    """The small-T kernel (a chain's k steps split over four waves, the
+    accumulator handed on) gives the grouped path's bits."""
+    shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=heads, head_dim=hd)
+    g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, 7 * T + d, torch.bfloat16, "uniform").items()}
+    print(f"decode chain T={T} d={d} E={E} k={k} N={heads * hd}", flush=True)
+    monkeypatch.setenv("MOVA_DECODE_CHAIN", "1")
+    dec = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
+    monkeypatch.setenv("MOVA_DECODE_CHAIN", "0")
+    reg = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
+    monkeypatch.delenv("MOVA_DECODE_CHAIN")
+    grp = _run(g, k, heads, hd, {"MOVA_PATH": "grouped"}, monkeypatch)
+    for name, a, b, c in zip(("out", "idx", "w"), dec, reg, grp):
+        assert torch.equal(a, c), f"{name}: chain kernel differs from the grouped path"
+        assert torch.equal(b, c), f"{name}: decode kernel differs from the grouped path"
