@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // index order (the touched set is read from the routing); the weights stay in
 // registers across passes of 16 pairs.  Value experts only (w * SiLU(z)).
 constexpr int kChainMaxPairs = 64;  // T * k this kernel accepts
-constexpr int kChainAutoPairs = 32;  // T * k up to which it is the default
+constexpr int kChainAutoPairs = 16;  // T * k up to which it is the default
 
 template <int kQ>  // k steps per wave (at most)
 __global__ __launch_bounds__(256) void decode_chain_kernel(
@@ -352,14 +352,20 @@ static auto pick_decode_kernel(bool unroll4, bool pair32) {
 }
 
 // Narrow outputs (e.g. one GPU's share of the heads under tensor parallelism)
-// give too few 128-column workgroups to fill the GPU's two per CU: one
-// 16-column group per wave then doubles the workgroups (and the MFMA chains
-// running at once).  Each group's chain is the same either way, so are the
-// bits.  The SwiGLU epilogue needs a gate and an up group in one wave.
+// give too few 128-column workgroups to fill the GPU's two per CU, and so do
+// a few tokens, which touch few experts (at most T * k): one 16-column group
+// per wave then doubles the workgroups (and the MFMA chains running at once).
+// Each group's chain is the same either way, so are the bits.  The SwiGLU
+// epilogue needs a gate and an up group in one wave.
 template <int kMode>
 static hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   constexpr int kRound = 512;  // two workgroups per CU
-  bool narrow = (long long)a.E * ceil_div(a.N, 128) < kRound;
+  const long long slices = ceil_div(a.N, 128);
+  const long long busy = std::min<long long>(a.E, (long long)a.T * a.k) * slices;
+  // busy: at most this many 128-column workgroups have pairs.  Measured at
+  // d = 2560, N = 1024 (T = 8, 10, 12, 14: 43.7 vs 56.8, 52.1 vs 58.1, 58.6
+  // vs 59.0, 62.3 vs 61.3 us, narrow vs not), narrow while busy <= 384.
+  bool narrow = (long long)a.E * slices < kRound || busy <= 3 * kRound / 4;
   const char* force = getenv("MOVA_DECODE_GROUPS");  // 1 or 2 (tests, measurement)
   if (force != nullptr && (strcmp(force, "1") == 0 || strcmp(force, "2") == 0))
     narrow = force[0] == '1';
