@@ -18,6 +18,7 @@ bytes = touched experts' weights once + router weights + x + out.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -98,9 +99,10 @@ def graph_time(calls, steps, warmup):
     return t1 - t0, reps * per_graph
 
 
-def run_single_layer(name, steps, warmup, copies):
+def run_single_layer(name, steps, warmup, copies, T=None):
+    """One layer of a named workload (T overrides its token count)."""
     w = inputs.WORKLOADS[name]
-    sh = w.shape
+    sh = w.shape if T is None else dataclasses.replace(w.shape, T=T)
     x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
     cps = make_copies(sh, w.seed, w.dtype, w.bias, copies)
     out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
@@ -582,6 +584,14 @@ def main():
                                 "pool": "4096 blocks x 16 slots x [8, 128] bf16, distinct random "
                                         "slots, no contiguous output"}
         torch.cuda.empty_cache()
+        log("small-batch decode ...")
+        small = []
+        for T in (1, 4, 16):
+            rr = run_single_layer("decode", args.steps, args.warmup, args.copies, T=T)
+            small.append({"T": T, "us_per_call": 1e6 * rr["graph_seconds"] / rr["graph_calls"],
+                          "touched_experts": rr["touched"]})
+            torch.cuda.empty_cache()
+        line["small_batch_decode"] = small
         log("tensor-parallel shards ...")
         shards = []
         for tp in (2, 8):
