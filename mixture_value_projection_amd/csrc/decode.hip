@@ -228,51 +228,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 //
 // With a handful of tokens only a few experts are touched, so the kernel
 // above runs few workgroups, each walking its k loop in several rounds of
-// loads.  Here a workgroup owns one (touched expert, 16-column group), 80 KB
-// of weights at d = 2560: its 4 waves each load one quarter of the group's k
-// steps (weight and token fragments) into registers at once, and the MFMA
-// chain of the 16 x 16 output tile then runs through the quarters in order,
-// wave after wave, the fp32 accumulator handed on through LDS.  It is the
-// same chain as in the other kernels (same operands, same order), so the
-// bits are the same.  Workgroup i takes the (i / groups)-th touched expert in
-// index order (the touched set is read from the routing); the weights stay in
-// registers across passes of 16 pairs.  Value experts only (w * SiLU(z)).
+// loads.  Here a workgroup owns one (touched expert, column group): 16
+// columns, or a 16-column gate block and its up block for the SwiGLU
+// epilogue (80 or 160 KB of weights at d = 2560).  Its kWaves waves each load
+// their share of the k steps (weight and token fragments) into registers at
+// once, and the MFMA chain of every 16 x 16 output tile then runs through the
+// shares in order, wave after wave, the fp32 accumulators handed on through
+// LDS.  It is the same chain as in the other kernels (same operands, same
+// order), so the bits are the same.  Workgroup i takes the (i / groups)-th
+// touched expert in index order (the touched set is read from the routing);
+// the weights stay in registers across passes of 16 pairs.  Epilogues as
+// decode_kernel's kMode.
 constexpr int kChainMaxPairs = 64;  // T * k this kernel accepts
-constexpr int kChainAutoPairs = 16;  // T * k up to which it is the default
 
-template <int kQ>  // k steps per wave (at most)
-__global__ __launch_bounds__(256) void decode_chain_kernel(
+template <int kQ, int kMode, int kWaves>  // kQ: k steps per wave (at most)
+__global__ __launch_bounds__(64 * kWaves) void decode_chain_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ idx, const float* __restrict__ topk_w,
-    f16_t* __restrict__ partial, int T, int d, int N, int E, int k) {
+    f16_t* __restrict__ partial, bf16_t* __restrict__ out_h, int T, int d, int N, int E, int k) {
+  constexpr int kG = kMode == kGemmRoutedSwiGLU ? 2 : 1;  // 16-column groups
   __shared__ int plist[kChainMaxPairs];
   __shared__ float wlist[kChainMaxPairs];
-  __shared__ f32x4 handoff[64];
-  __shared__ unsigned long long touched;
-  __shared__ int wave_hits[4];
+  __shared__ f32x4 handoff[kG][64];
+  __shared__ unsigned long long touched[2];  // E <= 128
+  __shared__ int wave_hits[kWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q = lane >> 4, r16 = lane & 15;
   const int npairs = T * k;  // <= kChainMaxPairs (launch condition)
-  const int groups = N / 16;
+  const int groups = N / (16 * kG);
   const int rank = blockIdx.x / groups;
-  const int n0 = (blockIdx.x % groups) * 16;
+  const int n0 = (blockIdx.x % groups) * 16 * kG;
 
-  // The routing, read once: the touched experts (E <= 64), this workgroup's
-  // one, and its pairs in pair order (one ballot round: npairs <= 64).
+  // The routing, read once: the touched experts, this workgroup's one, and
+  // its pairs in pair order (one ballot round: npairs <= 64).
   const bool in = tid < npairs;
   const int pe = in ? idx[tid] : -1;
   const float pwv = in ? topk_w[tid] : 0.f;
-  if (tid == 0) touched = 0ull;
+  if (tid < 2) touched[tid] = 0ull;
   __syncthreads();
-  if (pe >= 0 && pe < E) atomicOr(&touched, 1ull << pe);
+  if (pe >= 0 && pe < E) atomicOr(&touched[pe >> 6], 1ull << (pe & 63));
   __syncthreads();
-  uint64_t mask = touched;
-  if (rank >= __popcll(mask)) return;  // uniform across the workgroup
-  for (int i = 0; i < rank; ++i) mask &= mask - 1;
-  const int e = __ffsll((unsigned long long)mask) - 1;
+  const uint64_t m0 = touched[0], m1 = touched[1];
+  const int c0 = __popcll(m0);
+  if (rank >= c0 + __popcll(m1)) return;  // uniform across the workgroup
+  uint64_t m = rank < c0 ? m0 : m1;
+  for (int i = rank < c0 ? rank : rank - c0; i > 0; --i) m &= m - 1;
+  const int e = (rank < c0 ? 0 : 64) + __ffsll((unsigned long long)m) - 1;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const bool hit = pe == e;
   const uint64_t mm = __ballot(hit);
@@ -280,67 +284,108 @@ __global__ __launch_bounds__(256) void decode_chain_kernel(
   __syncthreads();
   int before = 0;
   for (int w = 0; w < wave; ++w) before += wave_hits[w];
+  int ce = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) ce += wave_hits[w];
   if (hit) {
     const int slot = before + __popcll(mm & lt_mask);
     plist[slot] = tid;
     wlist[slot] = pwv;
   }
-  const int ce = (wave_hits[0] + wave_hits[1]) + (wave_hits[2] + wave_hits[3]);
   __syncthreads();
 
   // This wave's steps [s0, s0 + ns) of the chain.  Its weight fragments are
   // requested together with the first pass's token fragments (one round trip).
   const int steps = d / 32;
-  const int per = ceil_div(steps, 4);  // <= kQ (launch condition)
+  const int per = ceil_div(steps, kWaves);  // <= kQ (launch condition)
   const int s0 = min(steps, wave * per);
   const int ns = min(steps, s0 + per) - s0;
-  const bf16_t* wrow = W + ((size_t)e * N + n0 + r16) * d + q * 8;
-  Frag16 wf[kQ];
+  Frag16 wf[kG][kQ];
 #pragma unroll
-  for (int i = 0; i < kQ; ++i)
-    if (i < ns) wf[i].u = load16(wrow + (s0 + i) * 32);
+  for (int g = 0; g < kG; ++g) {
+    const bf16_t* wrow = W + ((size_t)e * N + n0 + g * 16 + r16) * d + q * 8;
+#pragma unroll
+    for (int i = 0; i < kQ; ++i)
+      if (i < ns) wf[g][i].u = load16(wrow + (s0 + i) * 32);
+  }
 
   for (int p0 = 0; p0 < ce; p0 += 16) {
     // Token fragments of this pass (MFMA row r16 = pair p0 + r16; rows past
     // the expert's pairs repeat its last pair and are never stored).
-    const bf16_t* xr = x + (size_t)(plist[min(p0 + r16, ce - 1)] / k) * d + q * 8;
+    const int pr = plist[min(p0 + r16, ce - 1)];
+    const bf16_t* xr = x + (size_t)(kMode == kGemmRoutedLinear ? pr : pr / k) * d + q * 8;
     Frag16 xf[kQ];
 #pragma unroll
     for (int i = 0; i < kQ; ++i)
       if (i < ns) xf[i].u = load16(xr + (s0 + i) * 32);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < 4; ++w) {
-      if (wave == w) {
-        if (w > 0) acc = handoff[lane];
+    f32x4 acc[kG];
 #pragma unroll
-        for (int i = 0; i < kQ; ++i)
-          if (i < ns) acc = mfma16x16x32(xf[i].h, wf[i].h, acc);
-        if (w < 3) handoff[lane] = acc;
+    for (int g = 0; g < kG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kWaves; ++w) {
+      if (wave == w) {
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+          if (w > 0) acc[g] = handoff[g][lane];
+#pragma unroll
+          for (int i = 0; i < kQ; ++i)
+            if (i < ns) acc[g] = mfma16x16x32(xf[i].h, wf[g][i].h, acc[g]);
+          if (w < kWaves - 1) handoff[g][lane] = acc[g];
+        }
       }
       __syncthreads();
     }
-    if (wave == 3) {
+    if (wave == kWaves - 1) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int r = p0 + q * 4 + v;
-        if (r < ce)
-          partial[(size_t)plist[r] * N + n0 + r16] = (f16_t)(wlist[r] * siluf(acc[v]));
+        if (r < ce) {
+          if constexpr (kMode == kGemmRoutedSwiGLU) {
+            out_h[(size_t)plist[r] * (N / 2) + n0 / 2 + r16] =
+                (bf16_t)(siluf(acc[0][v]) * acc[1][v]);
+          } else {
+            const float z = acc[0][v];
+            f16_t* dst = partial + (size_t)plist[r] * N + n0 + r16;
+            if constexpr (kMode == kGemmRoutedSilu) *dst = (f16_t)(wlist[r] * siluf(z));
+            else *dst = (f16_t)(wlist[r] * z);
+          }
+        }
       }
     }
   }
 }
 
-// Whether the chain kernel takes a call, and with how many steps per wave.
+// Whether the chain kernel takes a call: 0, or its k steps per wave.  The
+// SwiGLU epilogue holds two groups of weights, so it splits k over 8 waves.
+// T * k up to which it is the default, measured: the value experts (d =
+// 2560, N = 1024) at T = 1, 2, 4, 8 took 16.1 / 20.1 / 30.5 / 50.4 us against
+// 33.8 / 35.3 / 37.4 and 43.7 us for the streaming kernel with one column
+// group per wave; the FFN (100 experts of width 768, top-8) at T = 1, 2, 4, 8
+// 62 / 89 / 133 / 186 us against 114 / 125 / 150 / 175 us.
+static int chain_auto_pairs(int mode) { return mode == kGemmRoutedSilu ? 16 : 32; }
+static int chain_waves(int mode) { return mode == kGemmRoutedSwiGLU ? 8 : 4; }
 static int chain_steps_per_wave(const DecodeArgs& a) {
   const char* v = getenv("MOVA_DECODE_CHAIN");  // 0 / 1 force it off / on (tests, measurement)
   const bool force_off = v != nullptr && strcmp(v, "0") == 0;
   const bool force_on = v != nullptr && strcmp(v, "1") == 0;
-  const int per = ceil_div(a.d / 32, 4);
-  const bool fits = a.mode == kGemmRoutedSilu && (long long)a.T * a.k <= kChainMaxPairs &&
-                    a.E <= 64 && a.N % 16 == 0 && per <= 24;
+  const int per = ceil_div(a.d / 32, chain_waves(a.mode));
+  const int max_per = a.mode == kGemmRoutedSwiGLU ? 16 : 24;  // registers (two groups)
+  const bool fits = (long long)a.T * a.k <= kChainMaxPairs && a.E <= 128 &&
+                    a.N % (a.mode == kGemmRoutedSwiGLU ? 32 : 16) == 0 && per <= max_per;
   if (!fits || force_off) return 0;
-  if (!force_on && (long long)a.T * a.k > kChainAutoPairs) return 0;
+  if (!force_on && (long long)a.T * a.k > chain_auto_pairs(a.mode)) return 0;
   return per <= 8 ? 8 : per <= 16 ? 16 : 24;
+}
+
+template <int kMode, int kWaves>
+static hipError_t launch_chain(const DecodeArgs& a, int q, hipStream_t stream) {
+  constexpr int kG = kMode == kGemmRoutedSwiGLU ? 2 : 1;
+  const dim3 grid((unsigned)(std::min(a.E, a.T * a.k) * (a.N / (16 * kG))));
+  auto kern = q == 8 ? decode_chain_kernel<8, kMode, kWaves> : decode_chain_kernel<16, kMode, kWaves>;
+  if constexpr (kMode != kGemmRoutedSwiGLU)  // at most 16 steps per wave for SwiGLU
+    if (q == 24) kern = decode_chain_kernel<24, kMode, kWaves>;
+  kern<<<grid, 64 * kWaves, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial,
+                                          (bf16_t*)a.out_h, a.T, a.d, a.N, a.E, a.k);
+  return hipGetLastError();
 }
 
 template <int kMode, int kGroups>
@@ -384,11 +429,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.T > kDecodeMaxT || a.k > kMaxTopK || a.d % 64 != 0 || a.N % 64 != 0)
     return hipErrorInvalidValue;
   if (const int q = chain_steps_per_wave(a)) {
-    const dim3 grid((unsigned)(std::min(a.E, a.T * a.k) * (a.N / 16)));
-    auto kern = q == 8 ? decode_chain_kernel<8> : q == 16 ? decode_chain_kernel<16>
-                                                          : decode_chain_kernel<24>;
-    kern<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, a.T, a.d, a.N, a.E, a.k);
-    return hipGetLastError();
+    switch (a.mode) {
+      case kGemmRoutedSilu: return launch_chain<kGemmRoutedSilu, 4>(a, q, stream);
+      case kGemmRoutedSwiGLU:
+        if (a.out_h == nullptr) return hipErrorInvalidValue;
+        return launch_chain<kGemmRoutedSwiGLU, 8>(a, q, stream);
+      case kGemmRoutedLinear: return launch_chain<kGemmRoutedLinear, 4>(a, q, stream);
+      default: return hipErrorInvalidValue;
+    }
   }
   switch (a.mode) {
     case kGemmRoutedSilu: return launch_decode_mode<kGemmRoutedSilu>(a, stream);

@@ -263,3 +263,25 @@ def test_ffn_every_tile_shape(T, d, E, k, inter, inter_s, monkeypatch):
     monkeypatch.delenv("MOVA_PATH")
     for tile, out in outs.items():
         assert torch.equal(out, outs[FFN_TILES[0]]), f"{tile} differs from {FFN_TILES[0]}"
+
+
+@pytest.mark.parametrize("T,d,E,k,inter,inter_s", [(1, 2560, 100, 8, 768, 768), (2, 512, 128, 8, 128, 0),
+                                                   (8, 256, 12, 3, 64, 64), (5, 320, 100, 8, 64, 64)])
+def test_ffn_chain_kernel_bitwise(T, d, E, k, inter, inter_s, monkeypatch):
+    """The small-T chain kernel in the SwiGLU and weighted-linear modes
+    (E up to 128) gives the grouped path's bits."""
+    sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s)
+    say(f"ffn chain T={T} d={d} E={E} k={k} inter={inter} shared={inter_s}")
+    L, g = gpu_layer(sh, seed=3 * T + E)
+    res = {}
+    for tag, env in (("chain", {"MOVA_PATH": "decode", "MOVA_DECODE_CHAIN": "1"}),
+                     ("stream", {"MOVA_PATH": "decode", "MOVA_DECODE_CHAIN": "0"}),
+                     ("grouped", {"MOVA_PATH": "grouped"})):
+        for name, val in env.items():
+            monkeypatch.setenv(name, val)
+        res[tag] = run_ffn(g, sh)
+        for name in env:
+            monkeypatch.delenv(name)
+    for tag in ("chain", "stream"):
+        for name, a, b in zip(("out", "idx", "w"), res[tag], res["grouped"]):
+            assert torch.equal(a, b), f"{tag}: {name} differs from the grouped path"
