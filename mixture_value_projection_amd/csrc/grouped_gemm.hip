@@ -16,9 +16,9 @@
 // epilogue stores z rounded once to bf16 (the dense layers' plain v_proj,
 // section "So what does it cost?").
 //
-// Block tile BM x BN (256 x 256, 128 x 256 or 128 x 128), k steps of 64, 8
-// waves in a 2 x 4 grid (or 4 waves in 2 x 2 for 128 x 128), each wave owning
-// a BM/2 x BN/4 (or BM/2 x BN/2) sub-tile of 16x16x32 MFMA tiles.  Operand
+// Block tile BM x BN (352 x 256, 256 x 256, 128 x 256 or 128 x 128), k steps
+// of 64, 8 waves in a 2 x 4 grid (or 4 waves in 2 x 2 for 128 x 128), each
+// wave owning a BM/2 x BN/4 (or BM/2 x BN/2) sub-tile of 16x16x32 MFMA tiles.  Operand
 // tiles go global -> LDS with direct (global_load_lds) 16-byte loads into a
 // ring of LDS stages: with 2 stages the loads of step k+1 are in flight while
 // step k's MFMAs run, one barrier per step; with 3 or 4 stages (128 x 128
@@ -30,7 +30,7 @@
 // global chunk each lane loads.
 //
 // Tile choice (measured): grouped mode takes 128 x 128 (2 stages, two
-// workgroups per CU) or 256 x 256 by the experts' average row count
+// workgroups per CU), 256 x 256 or 352 x 256 by the experts' average row count
 // (gemm_tile_grouped); dense mode takes 256 x
 // 256 once those tiles fill the 256 CUs, else 128 x 128 with 4 stages when
 // the grid is a single round of workgroups and 2 stages otherwise.
@@ -67,7 +67,12 @@ struct Tile {
   static constexpr int kTileA = kBM * kRowBytes;
   static constexpr int kTileB = kBN * kRowBytes;
   static constexpr int kStage = kTileA + kTileB;  // per buffer
-  static constexpr int kLoadsA = kBM * kRowBytes / 1024 / kWaves;  // 1 KB direct loads per wave
+  // A 1 KB direct load fills one 8-row block.  The A blocks are split over
+  // the waves as evenly as whole blocks allow (352 rows: 44 blocks, six per
+  // wave, the last wave taking the two left over).
+  static constexpr int kBlocksA = kBM / 8;
+  static constexpr int kLoadsA = (kBlocksA + kWaves - 1) / kWaves;  // per wave, at most
+  static constexpr bool kEvenA = kBlocksA % kWaves == 0;
   static constexpr int kLoadsB = kBN * kRowBytes / 1024 / kWaves;
   static constexpr int kRowsW = kBM / kWM;  // rows per wave
   static constexpr int kColsW = kBN / kWN;  // columns per wave
@@ -91,8 +96,9 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Tile shapes a caller can force with MOVA_GEMM_TILE (tests, measurements).
-static bool forced_tile(GemmTile* t) {
+// Tile shapes a caller can force with MOVA_GEMM_TILE (tests, measurements);
+// 352 x 256 exists in the routed modes only (a dense call ignores it).
+static bool forced_tile(GemmTile* t, bool routed) {
   const char* force = getenv("MOVA_GEMM_TILE");
   if (force == nullptr) return false;
   static const struct {
@@ -100,35 +106,43 @@ static bool forced_tile(GemmTile* t) {
     GemmTile tile;
   } kTiles[] = {{"256x256", {256, 256, 8, 2}},   {"128x256", {128, 256, 8, 2}},
                 {"128x128", {128, 128, 8, 2}},   {"128x128s3", {128, 128, 8, 3}},
-                {"128x128s4", {128, 128, 8, 4}}, {"128x128w4", {128, 128, 4, 4}}};
+                {"128x128s4", {128, 128, 8, 4}}, {"128x128w4", {128, 128, 4, 4}},
+                {"352x256", {352, 256, 8, 2}}};
   for (const auto& c : kTiles)
-    if (strcmp(force, c.name) == 0) {
+    if (strcmp(force, c.name) == 0 && (routed || c.tile.bm != 352)) {
       *t = c.tile;
       return true;
     }
   return false;
 }
 
-GemmTile gemm_tile_grouped(int T, int k, int E) {
+GemmTile gemm_tile_grouped(int T, int k, int E, int N) {
   GemmTile t;
-  if (forced_tile(&t)) return t;
+  if (forced_tile(&t, true)) return t;
   // By the experts' average row count R = T k / E.  Which tile wins depends
-  // on how each rounds the experts' rows up to whole M-tiles and the tiles up
-  // to whole rounds of workgroups (two 128 x 128 or one 256 x 256 per CU), so
-  // it alternates; measured on the value layer (d = 2560, N = 1024, E = 64,
-  // seeded uniform routing), call times in us:
-  //   R        48   96   128  192  224  256  288  320  384  448  512
-  //   128x128  100  115  150  154  188  196  207  235  247  281  300
-  //   256x256  114  119  124  137  201  197  209  212  218  285  289
-  // 128 x 128 up to R = 112 and from 209 to 304, 256 x 256 elsewhere.
+  // on how the busiest expert's rows (about 1.2-1.3 R under near-uniform
+  // routing) round up to whole M-tiles, and the tiles up to whole rounds of
+  // workgroups (two 128 x 128, or one 256 x 256 or 352 x 256, per CU); a
+  // tile tall enough to keep every expert within n M-tiles finishes in n
+  // rounds when the experts' 256-column tiles fill the CUs.  Measured on the
+  // value layer (d = 2560, N = 1024, E = 64, seeded uniform routing), call
+  // times in us:
+  //   R        48   96   128  192  208  224  256  272  288  320  384  448  512  576  640
+  //   128x128  100  115  150  154  -    188  196  208  207  235  247  281  300  -    -
+  //   256x256  114  119  124  137  202  201  197  -    209  212  218  285  289  299  350
+  //   352x256  -    -    -    152  172  150  159  172  239  243  251  256  262  355  358
+  // 352 x 256 for R in (200, 272] and (408, 560] when E * N / 256 >= 256;
+  // otherwise 128 x 128 up to R = 112 and from 209 to 304, 256 x 256 elsewhere.
   const long long R = ((long long)T * k + E / 2) / E;
+  const bool fills = (long long)E * ceil_div(N, 256) >= 256;
+  if (fills && ((R > 200 && R <= 272) || (R > 408 && R <= 560))) return {352, 256, 8, 2};
   if (R <= 112 || (R > 208 && R <= 304)) return {128, 128, 8, 2};
   return {256, 256, 8, 2};
 }
 
 GemmTile gemm_tile_grouped_ffn(int T, int k, int E) {
   GemmTile t;
-  if (forced_tile(&t)) return t;
+  if (forced_tile(&t, true)) return t;
   // The FFN's experts (E = 100, k = 8, 1536 / 2560 columns), the same kind
   // of alternation as above; call times in us:
   //   R        20   82   123  164  246  328  492   655
@@ -162,8 +176,10 @@ __device__ __forceinline__ void issue_loads(const TileCtx<MOVA_TILE_ARGS>& c, ch
   using TL = Tile<MOVA_TILE_ARGS>;
 #pragma unroll
   for (int i = 0; i < TL::kLoadsA; ++i)
-    __builtin_amdgcn_global_load_lds((const void*)(c.a_src[i] + k_byte),
-                                     (lds_void*)(stage + (wave * TL::kLoadsA + i) * 1024), 16, 0, 0);
+    if (TL::kEvenA || wave * TL::kLoadsA + i < TL::kBlocksA)  // wave-uniform
+      __builtin_amdgcn_global_load_lds((const void*)(c.a_src[i] + k_byte),
+                                       (lds_void*)(stage + (wave * TL::kLoadsA + i) * 1024), 16, 0,
+                                       0);
 #pragma unroll
   for (int i = 0; i < TL::kLoadsB; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(c.b_src[i] + k_byte),
@@ -223,6 +239,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
   constexpr bool kDense = !mode_routed(kMode);
   constexpr int WN = TL::kColsW;  // columns per wave
   static_assert(!mode_swiglu(kMode) || WN % 32 == 0, "SwiGLU pairs 16-column tiles");
+  static_assert(TL::kEvenA || kS == 2, "the ring's wait counts assume equal loads per wave");
   extern __shared__ __attribute__((aligned(1024))) char smem[];  // kS stages
   __shared__ int tile_pair[kDense ? 1 : kBM];
   __shared__ float tile_w[kDense ? 1 : kBM];
@@ -422,6 +439,7 @@ hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) 
 template <int kMode>
 static hipError_t launch_routed_mode(const GemmArgs& a, long long ub, hipStream_t stream) {
   const GemmTile t = a.tile;
+  if (t.bm == 352 && t.bn == 256) return launch_tiles<352, 256, 2, 4, 2, kMode>(a, ub, stream);
   if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, kMode>(a, ub, stream);
   if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, kMode>(a, ub, stream);
   if (t.bm == 128 && t.bn == 128 && t.waves == 8) {
@@ -446,7 +464,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
 
 GemmTile gemm_tile_dense(int T, int N) {
   GemmTile t;
-  if (forced_tile(&t)) return t;
+  if (forced_tile(&t, false)) return t;
   // 256 x 256 once those tiles fill the 256 CUs; below that 128 x 128, with
   // a 4-stage ring when the grid is a single round of workgroups (one per
   // CU, so the ring is what keeps loads in flight), else 2 stages (two

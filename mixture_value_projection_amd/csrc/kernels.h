@@ -96,7 +96,7 @@ struct GemmArgs {
   int mode = kGemmRoutedSilu;
 };
 // Tile of the grouped GEMM for a call (the dispatch builds M-tiles of tile.bm rows).
-GemmTile gemm_tile_grouped(int T, int k, int E);
+GemmTile gemm_tile_grouped(int T, int k, int E, int N);
 GemmTile gemm_tile_grouped_ffn(int T, int k, int E);  // the FFN's experts
 // Upper bound on M-tiles of height bm for any routing of T tokens.
 int gemm_max_mtiles(int T, int k, int E, int bm);

@@ -423,7 +423,7 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
     DecodeArgs da{xb, wb, idx, w, partial, T, d, N, E, k};
     err = launch_decode(da, stream);
   } else {
-    const GemmTile tile = gemm_tile_grouped(T, k, E);
+    const GemmTile tile = gemm_tile_grouped(T, k, E, N);
     {
       StageScope sc(1, stream);
       DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, router_tile_tokens(T), tile.bm};

@@ -236,7 +236,7 @@ def test_ffn_concurrent_host_threads():
     assert not errors, errors
 
 
-FFN_TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4"]
+FFN_TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4", "352x256"]
 
 
 @pytest.mark.parametrize("T,d,E,k,inter,inter_s", [(300, 512, 12, 4, 128, 64), (700, 320, 20, 8, 64, 0)])

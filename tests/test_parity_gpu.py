@@ -104,7 +104,7 @@ def test_ragged_shapes_both_paths(T, d, E, k, H, D):
         assert torch.equal(a[0], b[0])
 
 
-GEMM_TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4"]
+GEMM_TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4", "352x256"]
 
 
 @pytest.mark.parametrize("T,d,E,k,H,D", [(200, 512, 16, 4, 2, 64), (700, 320, 33, 3, 3, 64),

@@ -20,7 +20,7 @@ import paritylib as P
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4"]
+TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4", "352x256"]
 
 
 def say(msg):
