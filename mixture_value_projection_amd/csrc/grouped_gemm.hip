@@ -36,7 +36,9 @@
 // the grid is a single round of workgroups and 2 stages otherwise.
 //
 // A tile whose valid rows end in the upper half keeps its lower waves in the
-// k loop for the loads and barriers only (no MFMA work on empty rows).
+// k loop for the loads and barriers only (no MFMA work on empty rows); with 2
+// stages, a wave whose valid rows fit in half of its row blocks computes only
+// that half.
 //
 // Work order: routed modes map tile id -> (expert, n-tile, m-tile), m
 // fastest, so tiles that share an expert's weight slab are adjacent; dense
@@ -187,23 +189,25 @@ __device__ __forceinline__ void issue_loads(const TileCtx<MOVA_TILE_ARGS>& c, ch
                                      16, 0, 0);
 }
 
-// One k step (two 32-wide MFMA steps) of the wave's sub-tile.
-template <MOVA_TILE_PARAMS>
+// One k step (two 32-wide MFMA steps) of the wave's sub-tile, for its first
+// kUsed 16-row blocks (the rest hold no valid rows; their accumulators are
+// never stored).
+template <MOVA_TILE_PARAMS, int kUsed>
 __device__ __forceinline__ void mma_step(f32x4 (&acc)[kBM / kWM / 16][kBN / kWN / 16],
                                          const char* stage, int wm, int wn, int q, int r16) {
   using TL = Tile<MOVA_TILE_ARGS>;
-  constexpr int MI = TL::kMI, NJ = TL::kNJ;
+  constexpr int NJ = TL::kNJ;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int chunk = ks * 4 + q;
-    Frag16 fa[MI], fb[NJ];
+    Frag16 fa[kUsed], fb[NJ];
 #pragma unroll
-    for (int i = 0; i < MI; ++i) fa[i].u = load16(stage + swz(wm * TL::kRowsW + i * 16 + r16, chunk));
+    for (int i = 0; i < kUsed; ++i) fa[i].u = load16(stage + swz(wm * TL::kRowsW + i * 16 + r16, chunk));
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       fb[j].u = load16(stage + TL::kTileA + swz(wn * TL::kColsW + j * 16 + r16, chunk));
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < kUsed; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(fa[i].h, fb[j].h, acc[i][j]);
   }
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWN, wn = wave % kWN;
   const int q = lane >> 4, r16 = lane & 15;
 
@@ -321,21 +325,32 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     for (int j = 0; j < TL::kNJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = d / BK;
-  const bool active = wm * TL::kRowsW < rows;  // wave-uniform
+  // Valid 16-row blocks of this wave's rows (wave-uniform).
+  const int nv = min(TL::kMI, max(0, ceil_div(rows - wm * TL::kRowsW, 16)));
+  const bool active = nv > 0;
   if constexpr (kS == 2) {
     issue_loads<MOVA_TILE_ARGS>(c, smem, wave, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (active) {
+    // A wave whose valid rows fit in the first half of its row blocks runs
+    // a copy of the loop that computes only those (a separate loop, not a
+    // branch per block, keeps the register allocation of the full one).
+    auto steps = [&](auto used) {
       for (int kt = 0; kt < KT; ++kt) {
         char* cur = smem + (kt & 1) * TL::kStage;
         if (kt + 1 < KT)
           issue_loads<MOVA_TILE_ARGS>(c, smem + ((kt + 1) & 1) * TL::kStage, wave,
                                       (kt + 1) * kRowBytes);
-        mma_step<MOVA_TILE_ARGS>(acc, cur, wm, wn, q, r16);
+        mma_step<MOVA_TILE_ARGS, decltype(used)::value>(acc, cur, wm, wn, q, r16);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
+    };
+    constexpr int kHalf = (TL::kMI + 1) / 2;
+    if (nv > kHalf) {
+      steps(std::integral_constant<int, TL::kMI>{});
+    } else if (active) {
+      steps(std::integral_constant<int, kHalf>{});
     } else {
       for (int kt = 0; kt < KT; ++kt) {
         if (kt + 1 < KT)
@@ -368,7 +383,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
         raw_barrier();
         const int nk = kt + kS - 1;
         if constexpr (decltype(compute)::value)
-          mma_step<MOVA_TILE_ARGS>(acc, smem + (kt % kS) * TL::kStage, wm, wn, q, r16);
+          mma_step<MOVA_TILE_ARGS, TL::kMI>(acc, smem + (kt % kS) * TL::kStage, wm, wn, q, r16);
         issue_loads<MOVA_TILE_ARGS>(c, smem + (nk % kS) * TL::kStage, wave,
                                     min(nk, KT - 1) * kRowBytes);
       }
