@@ -150,9 +150,16 @@ GemmTile gemm_tile_grouped_ffn(int T, int k, int E) {
   //   R        20   82   123  164  246  328  492   655
   //   128x128  312  369  438  507  602  713  981   1225
   //   256x256  372  419  451  478  605  724  888   1130
-  // 128 x 128 up to R = 144 and from 209 to 384, 256 x 256 elsewhere.
+  // and measured again beside the 352 x 256 tile:
+  //   R        164  246  328  492
+  //   128x128  521  624  744  1009
+  //   256x256  495  620  740  920
+  //   352x256  505  569  665  963
+  // 128 x 128 up to R = 144, 352 x 256 from 209 to 352, 128 x 128 from 353
+  // to 384, 256 x 256 elsewhere.
   const long long R = ((long long)T * k + E / 2) / E;
-  if (R <= 144 || (R > 208 && R <= 384)) return {128, 128, 8, 2};
+  if (R > 208 && R <= 352) return {352, 256, 8, 2};
+  if (R <= 144 || (R > 352 && R <= 384)) return {128, 128, 8, 2};
   return {256, 256, 8, 2};
 }
 
