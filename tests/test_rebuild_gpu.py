@@ -117,3 +117,41 @@ def test_rebuild_all_slots_unused_is_zero():
     for path in ("grouped", "decode"):
         out = with_path(path, lambda: binding.value_from_routing(g["x"], gi, gw, g["expert_w"], H, D))
         assert torch.count_nonzero(out) == 0
+
+
+BOUNDARY_LOADS = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 95, 96, 97, 175, 176, 177, 191, 192,
+                  193, 271, 272, 273, 351, 352, 353]
+TILE_SHAPES = ["352x256", "256x256", "128x256", "128x128", "128x128s4", "128x128w4"]
+
+
+def test_tile_row_boundaries_every_tile():
+    """Experts whose row counts sit on either side of every tile's row-block,
+    half-tile and tile boundaries (16-row MFMA blocks; 32 / 64 / 96 / 176 / 192
+    / 272 rows, where a wave's valid rows stop fitting the first half of its
+    blocks; 128 / 256 / 352-row tiles), rebuilt from stored routing with the
+    tokens shuffled so that the gathered rows are scattered: every tile shape
+    against the oracle, and all with the same bits."""
+    E, k, d, H, D = len(BOUNDARY_LOADS), 1, 256, 5, 64
+    T = sum(BOUNDARY_LOADS)
+    rng = np.random.default_rng(77)
+    idx = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), BOUNDARY_LOADS)).reshape(T, k)
+    w = np.ones((T, k), dtype=np.float32)  # keeps |out| inside the parity rules' range
+    shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=H, head_dim=D)
+    g = P.to_gpu_inputs(inputs.make_layer(shape, 91, torch.bfloat16, "uniform"))
+    gi = torch.as_tensor(idx, device=DEV)
+    gw = torch.as_tensor(w, device=DEV)
+    o = P.oracle_inputs(g)
+    ref = oracle.rebuild_values(o["x"], o["expert_w"], idx, w)
+    outs = {}
+    try:
+        for tile in TILE_SHAPES:
+            os.environ["MOVA_GEMM_TILE"] = tile
+            say(f"row boundaries: tile {tile}, T={T} E={E} d={d} N={H * D}")
+            out = with_path("grouped", lambda: binding.value_from_routing(g["x"], gi, gw,
+                                                                          g["expert_w"], H, D))
+            say(f"  {P.check_output(out.reshape(T, -1), ref, what=f'tile {tile}')}")
+            outs[tile] = out
+    finally:
+        os.environ.pop("MOVA_GEMM_TILE", None)
+    for tile, out in outs.items():
+        assert torch.equal(out, outs[TILE_SHAPES[0]]), f"{tile} differs from {TILE_SHAPES[0]}"
