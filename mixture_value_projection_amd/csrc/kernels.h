@@ -65,9 +65,10 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 // ids outside [0, E) are not counted.
 hipError_t launch_dispatch_count(const DispatchArgs& a, hipStream_t stream);
 
-// Tile shape of the tiled GEMM: 256 x 256, 128 x 256 or 128 x 128 (rows x
-// columns), on 8 waves (2 x 4) or, for 128 x 128, also 4 waves (2 x 2), with
-// `stages` LDS buffers (2; 3 or 4 for 128 x 128).
+// Tile shape of the tiled GEMM: 352 x 256 (routed modes only), 256 x 256,
+// 128 x 256 or 128 x 128 (rows x columns), on 8 waves (2 x 4) or, for
+// 128 x 128, also 4 waves (2 x 2), with `stages` LDS buffers (2; 3 or 4 for
+// 128 x 128).
 struct GemmTile {
   int bm, bn, waves, stages;
 };
