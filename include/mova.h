@@ -253,7 +253,7 @@ int mova_dense_value_proj(const void* x, const void* w_v, int T, int d, int n_kv
  * The call is therefore ordered on `stream` as a whole, also when `stream` is
  * being captured into a graph.  The side stream is not used when `stream`
  * belongs to another device than the current one, when its first use would
- * fall inside a capture, or when the environment sets MOVA_SERIAL=1.  Calls
+ * fall inside a capture, or while MOVA_OVERRIDE_SERIAL is set.  Calls
  * from several host threads are safe; their shared experts share the one
  * side stream.
  */
@@ -275,6 +275,36 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
                          int inter_shared, int T, int d, float scale, void* out,
                          int32_t* topk_idx_out, float* topk_w_out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Kernel-choice overrides, for tests and measurements only.  A production
+ * call chooses its kernels from the shapes alone and reads no environment
+ * variable; an override set here forces one choice instead, for every later
+ * call in the process (all devices, all threads) until it is set back to 0
+ * (automatic).  A forced choice that a call's shape cannot take falls back
+ * to the automatic one.  Every choice computes the same results: the
+ * overrides exist so that tests can compare the kernels bit for bit and
+ * measurements can time each one.
+ */
+enum mova_override {
+  MOVA_OVERRIDE_PATH = 0,          /* 1: decode kernel (T <= 256), 2: dispatch + grouped GEMM */
+  MOVA_OVERRIDE_ROUTER = 1,        /* 1: tile router, 2 / 3: staged router, 32 / 64 tokens */
+  MOVA_OVERRIDE_GEMM_TILE = 2,     /* 1: 256x256, 2: 128x256, 3: 128x128, 4: 128x128 with 3
+                                      stages, 5: with 4 stages, 6: 128x128 on 4 waves,
+                                      7: 352x256 (routed GEMMs only) */
+  MOVA_OVERRIDE_DENSE_PATH = 3,    /* 1: split-k kernel (T <= 256), 2: tiled GEMM */
+  MOVA_OVERRIDE_DECODE_CHAIN = 4,  /* 1: chain kernel wherever it fits, 2: never */
+  MOVA_OVERRIDE_DECODE_GROUPS = 5, /* 1 or 2: 16-column groups per wave in the decode kernel */
+  MOVA_OVERRIDE_SERIAL = 6,        /* 1: the FFN's shared expert on the caller's stream */
+  MOVA_OVERRIDE_COUNT = 7
+};
+
+/* Sets an override; MOVA_OK, or MOVA_ERR_INVALID_ARG for an unknown key or a
+ * value outside the key's range (nothing changes then). */
+int mova_debug_override(int key, int value);
+
+/* The current value of an override (0 = automatic), -1 for an unknown key. */
+int mova_debug_override_get(int key);
 
 /*
  * Stage timing (profiling aid).  While enabled, each mova_value_forward call

@@ -63,6 +63,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mova_dense_workspace_bytes.argtypes = [i, i, i, i]
     lib.mova_dense_value_proj.restype = i
     lib.mova_dense_value_proj.argtypes = [vp, vp, i, i, i, i, vp, vp, sz, vp]
+    lib.mova_debug_override.restype = i
+    lib.mova_debug_override.argtypes = [i, i]
+    lib.mova_debug_override_get.restype = i
+    lib.mova_debug_override_get.argtypes = [i]
     lib.mova_timing_enable.restype = i
     lib.mova_timing_enable.argtypes = [i, ctypes.c_uint]
     lib.mova_timing_read.restype = i
@@ -363,6 +367,60 @@ def dense_value_proj(x: torch.Tensor, w_v: torch.Tensor, n_kv_heads: Optional[in
     if rc != MOVA_OK:
         raise MovaError(rc, "mova_dense_value_proj")
     return out
+
+
+# Kernel-choice overrides (mova_debug_override): name -> (key, {value name: value}).
+OVERRIDES = {
+    "path": (0, {"decode": 1, "grouped": 2}),
+    "router": (1, {"tile": 1, "staged32": 2, "staged64": 3}),
+    "gemm_tile": (2, {"256x256": 1, "128x256": 2, "128x128": 3, "128x128s3": 4,
+                      "128x128s4": 5, "128x128w4": 6, "352x256": 7}),
+    "dense_path": (3, {"skinny": 1, "tiled": 2}),
+    "decode_chain": (4, {"on": 1, "off": 2}),
+    "decode_groups": (5, {"1": 1, "2": 2}),
+    "serial": (6, {"on": 1}),
+}
+
+
+def set_override(name: str, value: Optional[str]) -> None:
+    """Force one kernel choice for later calls (tests, measurements); value
+    None restores the automatic choice."""
+    key, values = OVERRIDES[name]
+    v = 0 if value is None else values[str(value)]
+    rc = load_library().mova_debug_override(key, v)
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_debug_override")
+
+
+def get_override(name: str) -> Optional[str]:
+    key, values = OVERRIDES[name]
+    v = load_library().mova_debug_override_get(key)
+    return None if v == 0 else {i: n for n, i in values.items()}[v]
+
+
+def clear_overrides() -> None:
+    for name in OVERRIDES:
+        set_override(name, None)
+
+
+class overrides:
+    """Context manager: ``with overrides(path="grouped"): ...`` forces the
+    named choices inside the block and restores the previous ones after."""
+
+    def __init__(self, **kw):
+        self.kw = kw
+        self.saved = {}
+
+    def __enter__(self):
+        for name, value in self.kw.items():
+            self.saved[name] = get_override(name)
+            set_override(name, value)
+        return self
+
+    def __exit__(self, *exc):
+        for name, value in self.saved.items():
+            set_override(name, value)
+        return False
 
 
 def timing_enable(capacity: int, stages=STAGES) -> None:

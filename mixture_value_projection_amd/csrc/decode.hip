@@ -36,9 +36,6 @@
 // per CU (up to 256 registers per lane) the whole grid is resident at once.
 // The FFN's projections (100 experts, 1536 or 2560 columns) run in a few
 // rounds of workgroups.
-#include <stdlib.h>
-#include <string.h>
-
 #include <algorithm>
 #include <type_traits>
 
@@ -364,9 +361,8 @@ __global__ __launch_bounds__(64 * kWaves) void decode_chain_kernel(
 static int chain_auto_pairs(int mode) { return mode == kGemmRoutedSilu ? 16 : 32; }
 static int chain_waves(int mode) { return mode == kGemmRoutedSwiGLU ? 8 : 4; }
 static int chain_steps_per_wave(const DecodeArgs& a) {
-  const char* v = getenv("MOVA_DECODE_CHAIN");  // 0 / 1 force it off / on (tests, measurement)
-  const bool force_off = v != nullptr && strcmp(v, "0") == 0;
-  const bool force_on = v != nullptr && strcmp(v, "1") == 0;
+  const int ov = override_value(kOvDecodeChain);  // 1 / 2 force it on / off (tests, measurement)
+  const bool force_on = ov == 1, force_off = ov == 2;
   const int per = ceil_div(a.d / 32, chain_waves(a.mode));
   const int max_per = a.mode == kGemmRoutedSwiGLU ? 16 : 24;  // registers (two groups)
   const bool fits = (long long)a.T * a.k <= kChainMaxPairs && a.E <= 128 &&
@@ -411,9 +407,8 @@ static hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   // d = 2560, N = 1024 (T = 8, 10, 12, 14: 43.7 vs 56.8, 52.1 vs 58.1, 58.6
   // vs 59.0, 62.3 vs 61.3 us, narrow vs not), narrow while busy <= 384.
   bool narrow = (long long)a.E * slices < kRound || busy <= 3 * kRound / 4;
-  const char* force = getenv("MOVA_DECODE_GROUPS");  // 1 or 2 (tests, measurement)
-  if (force != nullptr && (strcmp(force, "1") == 0 || strcmp(force, "2") == 0))
-    narrow = force[0] == '1';
+  const int groups = override_value(kOvDecodeGroups);  // 1 or 2 (tests, measurement)
+  if (groups == 1 || groups == 2) narrow = groups == 1;
   narrow = narrow && kMode != kGemmRoutedSwiGLU;
   const dim3 grid(a.E * ceil_div(a.N, narrow ? 64 : 128));
   const bool unroll4 = (a.d / 32) % 4 == 0;

@@ -47,9 +47,6 @@
 // rows, not the weight, dominate what leaves L2).  Workgroups are dealt round
 // robin over the 8 XCDs; block b runs tile (b % 8) * per_xcd + b / 8, giving
 // each XCD one contiguous run of tiles (and its L2 the weights they share).
-#include <stdlib.h>
-#include <string.h>
-
 #include <type_traits>
 
 #include "common.h"
@@ -98,24 +95,19 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Tile shapes a caller can force with MOVA_GEMM_TILE (tests, measurements);
-// 352 x 256 exists in the routed modes only (a dense call ignores it).
+// Tile shapes the kOvGemmTile override can force (tests, measurements), by
+// its value 1 .. 7; 352 x 256 exists in the routed modes only (a dense call
+// ignores it).
 static bool forced_tile(GemmTile* t, bool routed) {
-  const char* force = getenv("MOVA_GEMM_TILE");
-  if (force == nullptr) return false;
-  static const struct {
-    const char* name;
-    GemmTile tile;
-  } kTiles[] = {{"256x256", {256, 256, 8, 2}},   {"128x256", {128, 256, 8, 2}},
-                {"128x128", {128, 128, 8, 2}},   {"128x128s3", {128, 128, 8, 3}},
-                {"128x128s4", {128, 128, 8, 4}}, {"128x128w4", {128, 128, 4, 4}},
-                {"352x256", {352, 256, 8, 2}}};
-  for (const auto& c : kTiles)
-    if (strcmp(force, c.name) == 0 && (routed || c.tile.bm != 352)) {
-      *t = c.tile;
-      return true;
-    }
-  return false;
+  static const GemmTile kTiles[] = {{256, 256, 8, 2}, {128, 256, 8, 2}, {128, 128, 8, 2},
+                                    {128, 128, 8, 3}, {128, 128, 8, 4}, {128, 128, 4, 4},
+                                    {352, 256, 8, 2}};
+  const int v = override_value(kOvGemmTile);
+  if (v < 1 || v > 7) return false;
+  const GemmTile c = kTiles[v - 1];
+  if (!routed && c.bm == 352) return false;
+  *t = c;
+  return true;
 }
 
 GemmTile gemm_tile_grouped(int T, int k, int E, int N) {

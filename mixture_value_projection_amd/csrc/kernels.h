@@ -25,6 +25,22 @@ inline hipError_t once_per_device(std::atomic<unsigned long long>& done, F set) 
   return e;
 }
 
+// Kernel-choice overrides (tests and measurements), set only through
+// mova_debug_override; 0 is the automatic choice.  Keys and values as the
+// mova_override enum of include/mova.h.  A relaxed atomic load: no call reads
+// the environment.
+enum OverrideKey {
+  kOvPath = 0,
+  kOvRouter = 1,
+  kOvGemmTile = 2,
+  kOvDensePath = 3,
+  kOvDecodeChain = 4,
+  kOvDecodeGroups = 5,
+  kOvSerial = 6,
+  kOvCount = 7
+};
+int override_value(int key);
+
 struct RouterArgs {
   const __bf16* x;
   const __bf16* wr;

@@ -1,10 +1,9 @@
 // C ABI of the MoVA routed value projection: argument checks, workspace
 // layout, path choice and launches.  Declarations and contracts: include/mova.h.
 #include <math.h>
-#include <stdlib.h>
-#include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -44,29 +43,35 @@ int check_heads(int n_kv_heads, int head_dim) {
 
 enum class Path { Decode, Grouped };
 
+// Kernel-choice overrides (mova_debug_override); largest value per key.
+std::atomic<int> g_override[kOvCount];
+constexpr int kOverrideMax[kOvCount] = {2, 3, 7, 2, 2, 2, 1};
+
+// Path forced by the kOvPath override: 1 the decode kernel (where T allows
+// it), 2 dispatch and the grouped GEMM; 0 when none applies.
+int forced_path(int T, Path* p) {
+  const int v = override_value(kOvPath);
+  if (v == 1 && T <= kDecodeMaxT) { *p = Path::Decode; return 1; }
+  if (v == 2) { *p = Path::Grouped; return 1; }
+  return 0;
+}
+
 Path choose_path(int T, int k) {
   (void)k;
-  const char* force = getenv("MOVA_PATH");
-  const bool decode_ok = T <= kDecodeMaxT;
-  if (force != nullptr) {
-    if (strcmp(force, "decode") == 0 && decode_ok) return Path::Decode;
-    if (strcmp(force, "grouped") == 0) return Path::Grouped;
-  }
-  return (T <= kDecodeAutoMaxT && decode_ok) ? Path::Decode : Path::Grouped;
+  Path p;
+  if (forced_path(T, &p)) return p;
+  return T <= kDecodeAutoMaxT ? Path::Decode : Path::Grouped;
 }
 
 // The FFN's routed experts take the decode kernel up to 1024 pairs (T = 128
 // at k = 8): measured at d = 2560, 100 experts of width 768, it is faster at
 // T = 64, level at 128 and slower from 192 on, where the experts average more
-// than 15 pairs.  MOVA_PATH forces either path, as for the value path.
+// than 15 pairs.  The kOvPath override forces either path, as for the value
+// path.
 Path choose_ffn_path(int T, int k) {
-  const char* force = getenv("MOVA_PATH");
-  const bool decode_ok = T <= kDecodeMaxT;
-  if (force != nullptr) {
-    if (strcmp(force, "decode") == 0 && decode_ok) return Path::Decode;
-    if (strcmp(force, "grouped") == 0) return Path::Grouped;
-  }
-  return (decode_ok && (long long)T * k <= 1024) ? Path::Decode : Path::Grouped;
+  Path p;
+  if (forced_path(T, &p)) return p;
+  return (T <= kDecodeMaxT && (long long)T * k <= 1024) ? Path::Decode : Path::Grouped;
 }
 
 // Workspace layout (every region 256-byte aligned):
@@ -113,12 +118,10 @@ constexpr long long kMaxSlots = 1ll << 40;
 enum class DensePath { Skinny, Tiled };
 
 DensePath choose_dense_path(int T) {
-  const char* force = getenv("MOVA_DENSE_PATH");
   const bool skinny_ok = T <= kDenseSkinnyMaxT;
-  if (force != nullptr) {
-    if (strcmp(force, "skinny") == 0 && skinny_ok) return DensePath::Skinny;
-    if (strcmp(force, "tiled") == 0) return DensePath::Tiled;
-  }
+  const int v = override_value(kOvDensePath);  // 1 split-k, 2 tiled (tests, measurement)
+  if (v == 1 && skinny_ok) return DensePath::Skinny;
+  if (v == 2) return DensePath::Tiled;
   return skinny_ok ? DensePath::Skinny : DensePath::Tiled;
 }
 
@@ -193,12 +196,11 @@ std::mutex g_side_mu;
 std::vector<SideStream> g_side;  // by device
 
 // The side stream for work ordered after `stream`, or null (run on `stream`
-// itself): MOVA_SERIAL=1, a stream of another device than the current one,
-// a first use while `stream` is capturing, or a failure to create the
-// stream.  Call with g_side_mu held.
+// itself): the kOvSerial override set to 1, a stream of another device than
+// the current one, a first use while `stream` is capturing, or a failure to
+// create the stream.  Call with g_side_mu held.
 SideStream* side_stream_for(hipStream_t stream) {
-  const char* serial = getenv("MOVA_SERIAL");
-  if (serial != nullptr && strcmp(serial, "1") == 0) return nullptr;
+  if (override_value(kOvSerial) == 1) return nullptr;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
   if (stream != nullptr) {
@@ -311,6 +313,10 @@ void timing_free() {
 }
 
 }  // namespace
+
+int mova::override_value(int key) {
+  return (key >= 0 && key < kOvCount) ? g_override[key].load(std::memory_order_relaxed) : 0;
+}
 
 extern "C" {
 
@@ -659,6 +665,17 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
     err = launch_combine(ca, stream);
   }
   return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+}
+
+int mova_debug_override(int key, int value) {
+  if (key < 0 || key >= kOvCount || value < 0 || value > kOverrideMax[key])
+    return MOVA_ERR_INVALID_ARG;
+  g_override[key].store(value, std::memory_order_relaxed);
+  return MOVA_OK;
+}
+
+int mova_debug_override_get(int key) {
+  return (key >= 0 && key < kOvCount) ? g_override[key].load(std::memory_order_relaxed) : -1;
 }
 
 int mova_timing_enable(int capacity, unsigned stage_mask) {

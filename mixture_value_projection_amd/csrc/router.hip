@@ -491,14 +491,15 @@ static int tile_router_tokens(int T) { return T <= 8192 ? 16 : T <= 16384 ? 32 :
 //   T       4096  4608  6144  8192  16384  20480  28672  32768
 //   tile    17.2  28.4  28.9  28.8  38.4   47.9   48.8   48.6 us
 //   staged  21.8  22.6  24.3  24.8  33.1   49.4   58.2   59.6   (32 tokens)
-// so the staged router takes 4096 < T <= 18432.  MOVA_ROUTER=tile, staged32
-// or staged64 forces a kernel (measurement, tests).
+// so the staged router takes 4096 < T <= 18432.  The kOvRouter override
+// forces the tile router (1) or the staged router with 32 (2) or 64 (3)
+// tokens per workgroup (measurement, tests).
 static RouterChoice router_choice(int T) {
-  const char* v = getenv("MOVA_ROUTER");
-  if (v != nullptr) {
-    if (strcmp(v, "tile") == 0) return {false, tile_router_tokens(T)};
-    if (strcmp(v, "staged32") == 0) return {true, 32};
-    if (strcmp(v, "staged64") == 0) return {true, 64};
+  switch (override_value(kOvRouter)) {
+    case 1: return {false, tile_router_tokens(T)};
+    case 2: return {true, 32};
+    case 3: return {true, 64};
+    default: break;
   }
   if (T > 4096 && T <= 18432) return {true, 32};
   return {false, tile_router_tokens(T)};

@@ -71,16 +71,14 @@ def test_workspace_bytes(lib):
 
 
 @pytest.mark.parametrize("T", [100, 4096, 5000, 8192, 20000, 40000])
-def test_workspace_bytes_independent_of_kernel_choice(T, monkeypatch):
+def test_workspace_bytes_independent_of_kernel_choice(T):
     """The workspace size depends on the shapes alone, not on which router or
     expert kernel a call will take (the switches that force them)."""
     want = binding.workspace_bytes(T, 2560, 64, 4, 8, 128)
-    for var, val in [("MOVA_ROUTER", "tile"), ("MOVA_ROUTER", "staged32"),
-                     ("MOVA_ROUTER", "staged64"), ("MOVA_PATH", "grouped"),
-                     ("MOVA_PATH", "decode"), ("MOVA_GEMM_TILE", "128x128")]:
-        monkeypatch.setenv(var, val)
-        assert binding.workspace_bytes(T, 2560, 64, 4, 8, 128) == want, (var, val)
-        monkeypatch.delenv(var)
+    for name, val in [("router", "tile"), ("router", "staged32"), ("router", "staged64"),
+                      ("path", "grouped"), ("path", "decode"), ("gemm_tile", "128x128")]:
+        with binding.overrides(**{name: val}):
+            assert binding.workspace_bytes(T, 2560, 64, 4, 8, 128) == want, (name, val)
 
 
 def fwd(lib, **kw):
@@ -281,3 +279,26 @@ def test_binding_rejects_wrong_dtype_on_cpu():
     x = torch.zeros(4, 64, dtype=torch.float32)
     with pytest.raises(ValueError):
         binding.route(x, torch.zeros(8, 64, dtype=torch.bfloat16), None, 2)
+
+
+def test_kernel_choice_overrides():
+    """mova_debug_override: range checks, round trip, and the binding's
+    context manager restoring the automatic choice; no environment variable
+    is consulted by the library."""
+    lib = binding.load_library()
+    for key in range(7):
+        assert lib.mova_debug_override_get(key) == 0
+    assert lib.mova_debug_override_get(7) == -1
+    assert lib.mova_debug_override_get(-1) == -1
+    assert lib.mova_debug_override(7, 1) == -1
+    assert lib.mova_debug_override(0, 3) == -1      # path takes 0..2
+    assert lib.mova_debug_override(2, 8) == -1      # seven tile shapes
+    assert lib.mova_debug_override(0, -1) == -1
+    assert lib.mova_debug_override_get(0) == 0       # a rejected value changes nothing
+    with binding.overrides(path="grouped", gemm_tile="352x256"):
+        assert lib.mova_debug_override_get(0) == 2
+        assert lib.mova_debug_override_get(2) == 7
+        assert binding.get_override("gemm_tile") == "352x256"
+    assert lib.mova_debug_override_get(0) == 0 and lib.mova_debug_override_get(2) == 0
+    with open(binding.LIBPATH, "rb") as fh:
+        assert b"getenv" not in fh.read(), "the library must not read the environment"

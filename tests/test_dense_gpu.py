@@ -1,12 +1,11 @@
 """Dense value projection (the matched GQA baseline) vs the CPU oracle.
 
 Both kernels are covered on every shape they accept: the split-k kernel (up
-to 256 tokens) and the tiled GEMM, forced with MOVA_DENSE_PATH.  Shapes span
+to 256 tokens) and the tiled GEMM, forced with the dense_path override.  Shapes span
 several tiles with ragged tails in T, d and N; the decode and prefill
 workloads run at full size, the 32768-token prefill on sampled rows.
 Acceptance rules: ``paritylib.check_dense_output``.
 """
-import os
 import sys
 
 import numpy as np
@@ -31,8 +30,8 @@ def _gpu_only():
     assert torch.cuda.is_available(), "GPU test run without a GPU"
     binding.load_library()
     yield
-    os.environ.pop("MOVA_DENSE_PATH", None)
-    os.environ.pop("MOVA_GEMM_TILE", None)
+    binding.set_override("dense_path", None)
+    binding.set_override("gemm_tile", None)
 
 
 def dense_inputs(T, d, N, seed):
@@ -44,12 +43,12 @@ def dense_inputs(T, d, N, seed):
 
 def run_dense(x, w, path=None):
     if path is None:
-        os.environ.pop("MOVA_DENSE_PATH", None)
+        binding.set_override("dense_path", None)
     else:
-        os.environ["MOVA_DENSE_PATH"] = path
+        binding.set_override("dense_path", path)
     out = binding.dense_value_proj(x, w, n_kv_heads=w.shape[0] // 64, head_dim=64)
     torch.cuda.synchronize()
-    os.environ.pop("MOVA_DENSE_PATH", None)
+    binding.set_override("dense_path", None)
     return out.reshape(x.shape[0], -1)
 
 
@@ -110,10 +109,10 @@ def test_dense_every_tile_shape(T, d, N):
     ref = ref_rows(x, w)
     outs = {}
     for tile in ("256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128w4"):
-        os.environ["MOVA_GEMM_TILE"] = tile
+        binding.set_override("gemm_tile", tile)
         say(f"dense tile {tile}: T={T} d={d} N={N}")
         outs[tile] = run_dense(x, w, "tiled")
-        os.environ.pop("MOVA_GEMM_TILE", None)
+        binding.set_override("gemm_tile", None)
         say(f"  {P.check_dense_output(outs[tile], ref, what=f'dense tile {tile}')}")
     for tile, o in outs.items():
         assert torch.equal(o, outs["256x256"]), f"{tile} differs from 256x256"

@@ -102,17 +102,17 @@ def _layer(T, d, E, k, heads, hd, seed, mode):
     return g
 
 
-def _run(g, k, heads, hd, env, monkeypatch):
-    for name, val in env.items():
-        monkeypatch.setenv(name, val)
+def _run(g, k, heads, hd, forced):
+    for name, val in forced.items():
+        binding.set_override(name, val)
     T = g["x"].shape[0]
     idx = torch.full((T, k), -7, dtype=torch.int32, device=DEV)
     w = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
     out = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, 2.5, heads,
                                 hd, topk_idx=idx, topk_w=w)
     torch.cuda.synchronize()
-    for name in env:
-        monkeypatch.delenv(name)
+    for name in forced:
+        binding.set_override(name, None)
     return out, idx, w
 
 
@@ -126,15 +126,15 @@ def _run(g, k, heads, hd, env, monkeypatch):
     (256, 512, 64, 4, 1, 128, "one_expert"),
     (250, 1024, 7, 3, 1, 64, "one_expert"),
 ])
-def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode, monkeypatch):
+def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode):
     """The decode path (two-kernel router, weight-streaming experts) and the
     grouped path (tile router, dispatch, grouped GEMM) give the same routing,
     weights and output bits, also with tied scores and with every token on
     one expert."""
     g = _layer(T, d, E, k, heads, hd, seed=T + E, mode=mode)
     print(f"paths T={T} d={d} E={E} k={k} N={heads * hd} {mode}", flush=True)
-    dec = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
-    grp = _run(g, k, heads, hd, {"MOVA_PATH": "grouped"}, monkeypatch)
+    dec = _run(g, k, heads, hd, {"path": "decode"})
+    grp = _run(g, k, heads, hd, {"path": "grouped"})
     for name, a, b in zip(("out", "idx", "w"), dec, grp):
         assert torch.equal(a, b), f"{name}: decode path differs from the grouped path"
     if mode == "ties":
@@ -151,24 +151,24 @@ def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode, monkeypat
 
 @pytest.mark.parametrize("T,d,E,k", [(4096, 2560, 64, 4), (1000, 320, 40, 8), (777, 192, 7, 3),
                                      (8192, 2560, 64, 4), (33, 2560, 64, 6)])
-def test_staged_router_bitwise(T, d, E, k, monkeypatch):
+def test_staged_router_bitwise(T, d, E, k):
     """The staged-weight router (32- or 64-token workgroups, the weight shared
     through LDS) gives the tile router's routing bits, and the grouped path
     built on its dispatch chunks gives the same output bits."""
     shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=1, head_dim=64)
     g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, T + d, torch.bfloat16, "uniform").items()}
-    monkeypatch.setenv("MOVA_PATH", "grouped")
+    binding.set_override("path", "grouped")
     res = {}
     for kind in ("tile", "staged32", "staged64"):
-        monkeypatch.setenv("MOVA_ROUTER", kind)
+        binding.set_override("router", kind)
         print(f"router {kind} T={T} d={d} E={E} k={k}", flush=True)
         idx, w = binding.route(g["x"], g["router_w"], g["router_b"], k, 2.5)
         out = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, 2.5,
                                     1, 64)
         torch.cuda.synchronize()
         res[kind] = (idx, w, out)
-    monkeypatch.delenv("MOVA_ROUTER", raising=False)
-    monkeypatch.delenv("MOVA_PATH")
+    binding.set_override("router", None)
+    binding.set_override("path", None)
     for kind in ("staged32", "staged64"):
         for name, a, b in zip(("idx", "w", "out"), res[kind], res["tile"]):
             assert torch.equal(a, b), f"{kind}: {name} differs from the tile router"
@@ -178,17 +178,17 @@ def test_staged_router_bitwise(T, d, E, k, monkeypatch):
 @pytest.mark.parametrize("T,d,E,k,heads,hd", [(64, 2560, 64, 4, 1, 128), (64, 2560, 64, 4, 4, 128),
                                               (100, 512, 16, 3, 3, 64), (256, 256, 40, 8, 1, 64),
                                               (7, 320, 5, 2, 2, 32)])
-def test_decode_column_groups_bitwise(groups, T, d, E, k, heads, hd, monkeypatch):
+def test_decode_column_groups_bitwise(groups, T, d, E, k, heads, hd):
     """The decode kernel with one or two 16-column groups per wave (narrow
     outputs, e.g. one GPU's share of the heads, take one) gives the grouped
     path's bits."""
     shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=heads, head_dim=hd)
     g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, T + E + heads, torch.bfloat16, "uniform").items()}
     print(f"decode groups={groups} T={T} d={d} E={E} k={k} N={heads * hd}", flush=True)
-    monkeypatch.setenv("MOVA_DECODE_GROUPS", groups)
-    dec = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
-    monkeypatch.delenv("MOVA_DECODE_GROUPS")
-    grp = _run(g, k, heads, hd, {"MOVA_PATH": "grouped"}, monkeypatch)
+    binding.set_override("decode_groups", groups)
+    dec = _run(g, k, heads, hd, {"path": "decode"})
+    binding.set_override("decode_groups", None)
+    grp = _run(g, k, heads, hd, {"path": "grouped"})
     for name, a, b in zip(("out", "idx", "w"), dec, grp):
         assert torch.equal(a, b), f"{name}: decode ({groups} groups) differs from the grouped path"
 
@@ -197,18 +197,18 @@ def test_decode_column_groups_bitwise(groups, T, d, E, k, heads, hd, monkeypatch
                                               (8, 2560, 64, 8, 8, 128), (16, 3072, 64, 4, 2, 128),
                                               (5, 64, 7, 3, 1, 64), (2, 256, 64, 1, 1, 128),
                                               (16, 512, 40, 4, 4, 64)])
-def test_decode_chain_kernel_bitwise(T, d, E, k, heads, hd, monkeypatch):
+def test_decode_chain_kernel_bitwise(T, d, E, k, heads, hd):
     """The small-T kernel (a chain's k steps split over four waves, the
     accumulator handed on) gives the grouped path's bits."""
     shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=heads, head_dim=hd)
     g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, 7 * T + d, torch.bfloat16, "uniform").items()}
     print(f"decode chain T={T} d={d} E={E} k={k} N={heads * hd}", flush=True)
-    monkeypatch.setenv("MOVA_DECODE_CHAIN", "1")
-    dec = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
-    monkeypatch.setenv("MOVA_DECODE_CHAIN", "0")
-    reg = _run(g, k, heads, hd, {"MOVA_PATH": "decode"}, monkeypatch)
-    monkeypatch.delenv("MOVA_DECODE_CHAIN")
-    grp = _run(g, k, heads, hd, {"MOVA_PATH": "grouped"}, monkeypatch)
+    binding.set_override("decode_chain", "on")
+    dec = _run(g, k, heads, hd, {"path": "decode"})
+    binding.set_override("decode_chain", "off")
+    reg = _run(g, k, heads, hd, {"path": "decode"})
+    binding.set_override("decode_chain", None)
+    grp = _run(g, k, heads, hd, {"path": "grouped"})
     for name, a, b, c in zip(("out", "idx", "w"), dec, reg, grp):
         assert torch.equal(a, c), f"{name}: chain kernel differs from the grouped path"
         assert torch.equal(b, c), f"{name}: decode kernel differs from the grouped path"

@@ -136,7 +136,7 @@ def test_ffn_rows_do_not_depend_on_other_tokens():
     (100, 512, 100, 8, 128, 0),
     (200, 128, 1, 1, 64, 64),      # every token on one expert: 200 pairs, passes of 32
 ])
-def test_ffn_decode_and_grouped_paths_bitwise(T, d, E, k, inter, inter_s, monkeypatch):
+def test_ffn_decode_and_grouped_paths_bitwise(T, d, E, k, inter, inter_s):
     """Few tokens take the weight-streaming decode kernel for the routed
     experts; forcing the grouped GEMM instead gives the same bits."""
     sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s,
@@ -145,25 +145,25 @@ def test_ffn_decode_and_grouped_paths_bitwise(T, d, E, k, inter, inter_s, monkey
     L, g = gpu_layer(sh, seed=T + 7 * E)
     res = {}
     for path in ("decode", "grouped"):
-        monkeypatch.setenv("MOVA_PATH", path)
+        binding.set_override("path", path)
         res[path] = run_ffn(g, sh)
-    monkeypatch.delenv("MOVA_PATH")
+    binding.set_override("path", None)
     for name, a, b in zip(("out", "idx", "w"), res["decode"], res["grouped"]):
         assert torch.equal(a, b), f"{name}: decode path differs from the grouped path"
 
 
 @pytest.mark.parametrize("T", [64, 600])
-def test_ffn_shared_expert_side_stream(T, monkeypatch):
+def test_ffn_shared_expert_side_stream(T):
     """The shared expert runs on the library's side stream, overlapping the
     router and the routed experts; the result is the bits of running it on
-    the caller's stream (MOVA_SERIAL=1), also when the call is captured in a
+    the caller's stream (the serial override), also when the call is captured in a
     graph and replayed with other work in between."""
     sh = inputs.FfnShape(T=T, d=512, E=100, k=8, inter=128, inter_shared=256)
     say(f"ffn side stream T={T}")
     L, g = gpu_layer(sh, seed=T + 1)
-    monkeypatch.setenv("MOVA_SERIAL", "1")
+    binding.set_override("serial", "on")
     serial = run_ffn(g, sh)
-    monkeypatch.delenv("MOVA_SERIAL")
+    binding.set_override("serial", None)
     side = run_ffn(g, sh)
     for name, a, b in zip(("out", "idx", "w"), side, serial):
         assert torch.equal(a, b), f"{name}: side stream changed the result"
@@ -240,17 +240,17 @@ FFN_TILES = ["256x256", "128x256", "128x128", "128x128s3", "128x128s4", "128x128
 
 
 @pytest.mark.parametrize("T,d,E,k,inter,inter_s", [(300, 512, 12, 4, 128, 64), (700, 320, 20, 8, 64, 0)])
-def test_ffn_every_tile_shape(T, d, E, k, inter, inter_s, monkeypatch):
+def test_ffn_every_tile_shape(T, d, E, k, inter, inter_s):
     """The FFN's grouped GEMMs (SwiGLU gate/up, weighted down) in every tile
     shape: each against the oracle, and all of them with the same bits."""
     sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s)
     L, g = gpu_layer(sh, seed=T + E)
     o = {kk: v.double().numpy() for kk, v in L.items()}
     ref = oracle.route(o["x"], o["router_w"], o["router_b"], k, sh.scale)
-    monkeypatch.setenv("MOVA_PATH", "grouped")
+    binding.set_override("path", "grouped")
     outs = {}
     for tile in FFN_TILES:
-        monkeypatch.setenv("MOVA_GEMM_TILE", tile)
+        binding.set_override("gemm_tile", tile)
         say(f"ffn tile {tile}: T={T} d={d} E={E} k={k} inter={inter} shared={inter_s}")
         out, idx, w = run_ffn(g, sh)
         if tile == FFN_TILES[0]:
@@ -259,29 +259,29 @@ def test_ffn_every_tile_shape(T, d, E, k, inter, inter_s, monkeypatch):
             want = ffn_reference(L, sh, rows, rc.effective_idx, rc.effective_w)
             say(f"  {P.check_output(out, want, what=f'ffn tile {tile}')}")
         outs[tile] = out
-    monkeypatch.delenv("MOVA_GEMM_TILE")
-    monkeypatch.delenv("MOVA_PATH")
+    binding.set_override("gemm_tile", None)
+    binding.set_override("path", None)
     for tile, out in outs.items():
         assert torch.equal(out, outs[FFN_TILES[0]]), f"{tile} differs from {FFN_TILES[0]}"
 
 
 @pytest.mark.parametrize("T,d,E,k,inter,inter_s", [(1, 2560, 100, 8, 768, 768), (2, 512, 128, 8, 128, 0),
                                                    (8, 256, 12, 3, 64, 64), (5, 320, 100, 8, 64, 64)])
-def test_ffn_chain_kernel_bitwise(T, d, E, k, inter, inter_s, monkeypatch):
+def test_ffn_chain_kernel_bitwise(T, d, E, k, inter, inter_s):
     """The small-T chain kernel in the SwiGLU and weighted-linear modes
     (E up to 128) gives the grouped path's bits."""
     sh = inputs.FfnShape(T=T, d=d, E=E, k=k, inter=inter, inter_shared=inter_s)
     say(f"ffn chain T={T} d={d} E={E} k={k} inter={inter} shared={inter_s}")
     L, g = gpu_layer(sh, seed=3 * T + E)
     res = {}
-    for tag, env in (("chain", {"MOVA_PATH": "decode", "MOVA_DECODE_CHAIN": "1"}),
-                     ("stream", {"MOVA_PATH": "decode", "MOVA_DECODE_CHAIN": "0"}),
-                     ("grouped", {"MOVA_PATH": "grouped"})):
+    for tag, env in (("chain", {"path": "decode", "decode_chain": "on"}),
+                     ("stream", {"path": "decode", "decode_chain": "off"}),
+                     ("grouped", {"path": "grouped"})):
         for name, val in env.items():
-            monkeypatch.setenv(name, val)
+            binding.set_override(name, val)
         res[tag] = run_ffn(g, sh)
         for name in env:
-            monkeypatch.delenv(name)
+            binding.set_override(name, None)
     for tag in ("chain", "stream"):
         for name, a, b in zip(("out", "idx", "w"), res[tag], res["grouped"]):
             assert torch.equal(a, b), f"{tag}: {name} differs from the grouped path"

@@ -9,7 +9,6 @@ The pool is filled with a sentinel first.  Checks, on both execution paths
   and of a plain ``mova_value_forward`` call;
 * padding (-1) and out-of-pool slots store nothing; ``out`` may be omitted.
 """
-import os
 import sys
 
 import numpy as np
@@ -35,7 +34,7 @@ def _gpu_only():
     assert torch.cuda.is_available(), "GPU test run without a GPU"
     binding.load_library()
     yield
-    os.environ.pop("MOVA_PATH", None)
+    binding.set_override("path", None)
 
 
 def make_slots(T, num_slots, seed, pad_every=7):
@@ -60,7 +59,7 @@ def rows_of(t, idx, n):
 
 
 def run_paged(g, k, scale, H, D, pool, slots, path, with_out=True):
-    os.environ["MOVA_PATH"] = path
+    binding.set_override("path", path)
     T = g["x"].shape[0]
     out = torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV) if with_out else None
     idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
@@ -69,7 +68,7 @@ def run_paged(g, k, scale, H, D, pool, slots, path, with_out=True):
                                 pool, torch.as_tensor(slots, device=DEV), out=out,
                                 topk_idx=idx, topk_w=w)
     torch.cuda.synchronize()
-    os.environ.pop("MOVA_PATH", None)
+    binding.set_override("path", None)
     return out, idx, w
 
 
@@ -123,10 +122,10 @@ def test_paged_without_out_equals_plain_forward(path):
     say(f"paged no-out T={T} {path}")
     pool = torch.full((nb, bs, H, D), SENTINEL, dtype=torch.bfloat16, device=DEV)
     run_paged(g, k, 2.5, H, D, pool, slots, path, with_out=False)
-    os.environ["MOVA_PATH"] = path
+    binding.set_override("path", path)
     plain = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, 2.5, H, D)
     torch.cuda.synchronize()
-    os.environ.pop("MOVA_PATH", None)
+    binding.set_override("path", None)
     tok = np.nonzero((slots >= 0) & (slots < nb * bs))[0]
     assert torch.equal(rows_of(pool.reshape(nb * bs, -1), slots[tok], nb * bs),
                        rows_of(plain.reshape(T, -1), tok, T))

@@ -8,7 +8,6 @@ the decode step and prefill chunk in full, the skewed and chunked workloads
 with routing checked on every token and outputs on a seeded sample plus all
 near-tie tokens and the hottest expert's tokens.
 """
-import os
 import sys
 
 import numpy as np
@@ -33,22 +32,22 @@ def _gpu_only():
     assert torch.cuda.is_available(), "GPU test run without a GPU"
     binding.load_library()
     yield
-    os.environ.pop("MOVA_PATH", None)
-    os.environ.pop("MOVA_GEMM_TILE", None)
+    binding.set_override("path", None)
+    binding.set_override("gemm_tile", None)
 
 
 def run_forward(g, k, scale, H, D, path=None):
     if path is None:
-        os.environ.pop("MOVA_PATH", None)
+        binding.set_override("path", None)
     else:
-        os.environ["MOVA_PATH"] = path
+        binding.set_override("path", path)
     T = g["x"].shape[0]
     idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
     w = torch.empty(T, k, dtype=torch.float32, device=DEV)
     out = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, scale,
                                 H, D, topk_idx=idx, topk_w=w)
     torch.cuda.synchronize()
-    os.environ.pop("MOVA_PATH", None)
+    binding.set_override("path", None)
     return out, idx, w
 
 
@@ -116,10 +115,10 @@ def test_grouped_gemm_every_tile_shape(T, d, E, k, H, D):
     g, sh = layer(T, d, E, k, H, D, seed=T + 3 * E)
     outs = {}
     for tile in GEMM_TILES:
-        os.environ["MOVA_GEMM_TILE"] = tile
+        binding.set_override("gemm_tile", tile)
         say(f"grouped tile {tile}: T={T} d={d} E={E} k={k} H={H} D={D}")
         out, idx, w = run_forward(g, k, 2.5, H, D, "grouped")
-        os.environ.pop("MOVA_GEMM_TILE", None)
+        binding.set_override("gemm_tile", None)
         st = P.full_check(g, k, 2.5, H, D, out, idx, w, what=f"tile {tile}")
         say(f"  {st}")
         outs[tile] = out

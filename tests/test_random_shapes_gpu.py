@@ -7,7 +7,6 @@ seconds.  Value path: both execution paths where they apply and a drawn tile
 shape, checked against the oracle and against each other bit for bit.  Dense
 projection: both kernels where they apply.  FFN: routing and outputs.
 """
-import os
 import sys
 
 import numpy as np
@@ -33,8 +32,8 @@ def _gpu_only():
     assert torch.cuda.is_available(), "GPU test run without a GPU"
     binding.load_library()
     yield
-    for v in ("MOVA_PATH", "MOVA_GEMM_TILE", "MOVA_DENSE_PATH"):
-        os.environ.pop(v, None)
+    for v in ("path", "gemm_tile", "dense_path"):
+        binding.set_override(v, None)
 
 
 def value_shape(seed):
@@ -60,15 +59,15 @@ def test_value_forward_random_shape(seed):
     g = P.to_gpu_inputs(inputs.make_layer(shape, 50 + seed, torch.bfloat16, "uniform"))
     outs = {}
     for path in ["grouped"] + (["decode"] if T <= 256 else []):
-        os.environ["MOVA_PATH"] = path
-        os.environ["MOVA_GEMM_TILE"] = tile
+        binding.set_override("path", path)
+        binding.set_override("gemm_tile", tile)
         idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
         w = torch.empty(T, k, dtype=torch.float32, device=DEV)
         out = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, 2.5,
                                     H, D, topk_idx=idx, topk_w=w)
         torch.cuda.synchronize()
-        os.environ.pop("MOVA_PATH", None)
-        os.environ.pop("MOVA_GEMM_TILE", None)
+        binding.set_override("path", None)
+        binding.set_override("gemm_tile", None)
         st = P.full_check(g, k, 2.5, H, D, out, idx, w, what=f"seed {seed} {path}")
         say(f"  {path}: {st}")
         outs[path] = out
@@ -88,10 +87,10 @@ def test_dense_random_shape(seed):
                                                   head_dim=64), 60 + seed).to(DEV)
     ref = oracle.dense_value_proj(x.cpu().double().numpy(), w.cpu().double().numpy())
     for path in ["tiled"] + (["skinny"] if T <= 256 else []):
-        os.environ["MOVA_DENSE_PATH"] = path
+        binding.set_override("dense_path", path)
         out = binding.dense_value_proj(x, w, N // 64, 64).reshape(T, N)
         torch.cuda.synchronize()
-        os.environ.pop("MOVA_DENSE_PATH", None)
+        binding.set_override("dense_path", None)
         say(f"  {path}: {P.check_dense_output(out, ref, what=f'dense seed {seed} {path}')}")
 
 

@@ -7,7 +7,6 @@
   ``oracle.rebuild_values`` under the output parity rules, with the decode
   and grouped paths agreeing bit for bit.
 """
-import os
 import sys
 
 import numpy as np
@@ -32,17 +31,17 @@ def _gpu_only():
     assert torch.cuda.is_available(), "GPU test run without a GPU"
     binding.load_library()
     yield
-    os.environ.pop("MOVA_PATH", None)
+    binding.set_override("path", None)
 
 
 def with_path(path, fn):
-    os.environ["MOVA_PATH"] = path
+    binding.set_override("path", path)
     try:
         r = fn()
         torch.cuda.synchronize()
         return r
     finally:
-        os.environ.pop("MOVA_PATH", None)
+        binding.set_override("path", None)
 
 
 SHAPES = [
@@ -145,13 +144,13 @@ def test_tile_row_boundaries_every_tile():
     outs = {}
     try:
         for tile in TILE_SHAPES:
-            os.environ["MOVA_GEMM_TILE"] = tile
+            binding.set_override("gemm_tile", tile)
             say(f"row boundaries: tile {tile}, T={T} E={E} d={d} N={H * D}")
             out = with_path("grouped", lambda: binding.value_from_routing(g["x"], gi, gw,
                                                                           g["expert_w"], H, D))
             say(f"  {P.check_output(out.reshape(T, -1), ref, what=f'tile {tile}')}")
             outs[tile] = out
     finally:
-        os.environ.pop("MOVA_GEMM_TILE", None)
+        binding.set_override("gemm_tile", None)
     for tile, out in outs.items():
         assert torch.equal(out, outs[TILE_SHAPES[0]]), f"{tile} differs from {TILE_SHAPES[0]}"
