@@ -50,7 +50,8 @@ enum mova_status {
   MOVA_ERR_INVALID_ARG = -1, /* null pointer, negative size, misaligned pointer */
   MOVA_ERR_UNSUPPORTED = -2, /* shape outside the supported domain */
   MOVA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than mova_workspace_bytes */
-  MOVA_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+  MOVA_ERR_HIP = -4,         /* a HIP launch or runtime call failed */
+  MOVA_ERR_SCRATCH = -5      /* mova_value_forward_noalloc: shapes need more than its scratch */
 };
 
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */
@@ -173,6 +174,35 @@ int mova_value_from_routing(const void* x, const int32_t* topk_idx, const float*
                             const void* expert_w, int T, int d, int E, int k, int n_kv_heads,
                             int head_dim, void* out, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * mova_value_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, kernels, numerics and results (bit for bit) as
+ * mova_value_forward, without the workspace: the call takes its scratch from
+ * a static device array of MOVA_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on each device it runs on, from that device's first use until the
+ * process ends.  It calls no allocating routine.
+ *
+ * - Size limit: shapes whose mova_workspace_bytes(...) exceeds
+ *   MOVA_NOALLOC_SCRATCH_BYTES return MOVA_ERR_SCRATCH before anything is
+ *   enqueued (at d = 2560, E = 64, k = 4, N = 1024 that is T up to about
+ *   6100 tokens; the scratch is 48 MiB).
+ * - The scratch's contents on entry do not matter (each call writes what it
+ *   reads); it keeps the last call's contents.
+ * - Calls that overlap on one device share its one scratch array and race:
+ *   the caller orders them (one stream, or events between streams).
+ * - `stream` must belong to the current device (else MOVA_ERR_INVALID_ARG);
+ *   NULL is the current device's null stream.
+ * - Other errors as for mova_value_forward (MOVA_ERR_HIP also when the
+ *   scratch's device address cannot be looked up).
+ */
+#define MOVA_NOALLOC_SCRATCH_BYTES (48u << 20)
+
+int mova_value_forward_noalloc(const void* x, const void* router_w, const float* router_b,
+                               const void* expert_w, int T, int d, int E, int k, float scale,
+                               int n_kv_heads, int head_dim, void* out,
+                               int32_t* topk_idx_out, float* topk_w_out, hipStream_t stream);
 
 /*
  * Bytes of device workspace mova_dense_value_proj needs for these sizes: 0

@@ -50,6 +50,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mova_value_forward_paged.restype = i
     lib.mova_value_forward_paged.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, i, i, vp, vp,
                                              vp, vp, vp, sz, vp]
+    lib.mova_value_forward_noalloc.restype = i
+    lib.mova_value_forward_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, vp, vp]
     lib.mova_value_from_routing.restype = i
     lib.mova_value_from_routing.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, sz, vp]
     lib.mova_ffn_workspace_bytes.restype = sz
@@ -176,6 +178,45 @@ def value_forward(x: torch.Tensor, router_w: torch.Tensor, router_b: Optional[to
                                 workspace.numel(), _stream(dev))
     if rc != MOVA_OK:
         raise MovaError(rc, "mova_value_forward")
+    return out
+
+
+# Size of the static scratch of mova_value_forward_noalloc (MOVA_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 48 << 20
+
+
+def value_forward_noalloc(x: torch.Tensor, router_w: torch.Tensor,
+                          router_b: Optional[torch.Tensor], expert_w: torch.Tensor, k: int,
+                          scale: float, out: torch.Tensor,
+                          topk_idx: Optional[torch.Tensor] = None,
+                          topk_w: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mova_value_forward_noalloc: mova_value_forward with the library's static
+    scratch instead of a workspace.  ``out`` (bf16 [T, n_kv_heads, head_dim])
+    is required, so this wrapper allocates nothing either."""
+    lib = load_library()
+    T, d = x.shape
+    E, N, d2 = expert_w.shape
+    if d2 != d:
+        raise ValueError("expert_w's last dim must equal x's width")
+    if out.dim() != 3 or out.shape[1] * out.shape[2] != N:
+        raise ValueError("out must be [T, n_kv_heads, head_dim] with n_kv_heads * head_dim = N")
+    H, D = out.shape[1], out.shape[2]
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(router_w, "router_w", torch.bfloat16, (E, d), dev)
+    if router_b is not None:
+        _check(router_b, "router_b", torch.float32, (E,), dev)
+    _check(expert_w, "expert_w", torch.bfloat16, (E, N, d), dev)
+    _check(out, "out", torch.bfloat16, (T, H, D), dev)
+    if topk_idx is not None:
+        _check(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    if topk_w is not None:
+        _check(topk_w, "topk_w", torch.float32, (T, k), dev)
+    rc = lib.mova_value_forward_noalloc(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_w),
+                                        T, d, E, k, float(scale), H, D, _ptr(out), _ptr(topk_idx),
+                                        _ptr(topk_w), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_value_forward_noalloc")
     return out
 
 

@@ -312,6 +312,36 @@ void timing_free() {
   g_timing.mask = 0;
 }
 
+// ---- workspace of the entry point that allocates nothing -----------------
+//
+// mova_value_forward_noalloc takes its workspace from this array instead of
+// the caller.  Each device the library runs on holds its own copy, allocated
+// with the library's code object and kept until the process ends.  In host
+// code `scratch` names a host-side stand-in, not a device address: its
+// address on a device comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOVA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // by device ordinal; null until first use
+
+// This device's scratch address (looked up on the device's first call), or
+// null when the lookup fails.  `dev` must be the current device.
+void* device_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();  // clear the sticky error of the failed lookup
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 int mova::override_value(int key) {
@@ -329,6 +359,9 @@ const char* mova_status_str(int status) {
     case MOVA_ERR_UNSUPPORTED: return "MOVA_ERR_UNSUPPORTED: shape outside the supported domain";
     case MOVA_ERR_WORKSPACE: return "MOVA_ERR_WORKSPACE: workspace missing or too small";
     case MOVA_ERR_HIP: return "MOVA_ERR_HIP: a HIP launch or runtime call failed";
+    case MOVA_ERR_SCRATCH:
+      return "MOVA_ERR_SCRATCH: the call needs more than the library's static scratch "
+             "(MOVA_NOALLOC_SCRATCH_BYTES); use mova_value_forward with a workspace";
     default: return "MOVA: unknown status";
   }
 }
@@ -489,6 +522,33 @@ int mova_value_forward_paged(const void* x, const void* router_w, const float* r
   return value_forward_impl(x, router_w, router_b, expert_w, T, d, E, k, scale, n_kv_heads,
                             head_dim, out, &pg, topk_idx_out, topk_w_out, workspace,
                             workspace_bytes, stream);
+}
+
+int mova_value_forward_noalloc(const void* x, const void* router_w, const float* router_b,
+                               const void* expert_w, int T, int d, int E, int k, float scale,
+                               int n_kv_heads, int head_dim, void* out, int32_t* topk_idx_out,
+                               float* topk_w_out, hipStream_t stream) {
+  // Host-side checks first: nothing is looked up or enqueued for a call that
+  // fails them.
+  int rc = check_shape(T, d, E, k);
+  if (rc != MOVA_OK) return rc;
+  rc = check_heads(n_kv_heads, head_dim);
+  if (rc != MOVA_OK) return rc;
+  if (T == 0) return MOVA_OK;
+  const size_t need = layout(T, E, k, n_kv_heads * head_dim).total;
+  if (need > (size_t)MOVA_NOALLOC_SCRATCH_BYTES) return MOVA_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOVA_ERR_HIP;
+  if (stream != nullptr) {
+    hipDevice_t sdev = 0;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return MOVA_ERR_HIP;
+    if ((int)sdev != dev) return MOVA_ERR_INVALID_ARG;
+  }
+  void* ws = device_scratch(dev);
+  if (ws == nullptr) return MOVA_ERR_HIP;
+  return value_forward_impl(x, router_w, router_b, expert_w, T, d, E, k, scale, n_kv_heads,
+                            head_dim, out, nullptr, topk_idx_out, topk_w_out, ws,
+                            (size_t)MOVA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t mova_dense_workspace_bytes(int T, int d, int n_kv_heads, int head_dim) {

@@ -15,7 +15,7 @@ from mixture_value_projection_amd.build import LIBPATH
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mova.h")
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH = 0, -1, -2, -3, -4, -5
 FAKE = 1 << 20  # an aligned non-null address that is never dereferenced
 
 
@@ -302,3 +302,21 @@ def test_kernel_choice_overrides():
     assert lib.mova_debug_override_get(0) == 0 and lib.mova_debug_override_get(2) == 0
     with open(binding.LIBPATH, "rb") as fh:
         assert b"getenv" not in fh.read(), "the library must not read the environment"
+
+
+def test_noalloc_rejects_before_touching_the_gpu(lib):
+    """mova_value_forward_noalloc: shape errors and calls larger than the
+    static scratch are refused on the host (no device lookup, no launch)."""
+    def call(T, d=2560, E=64, k=4, H=8, D=128):
+        return lib.mova_value_forward_noalloc(FAKE, FAKE, None, FAKE, T, d, E, k, 2.5, H, D, FAKE,
+                                              None, None, None)
+    assert call(0) == OK
+    assert call(16, E=65) == UNSUPPORTED
+    assert call(16, d=2500) == UNSUPPORTED
+    assert call(-1) == INVALID
+    big = 1
+    while binding.workspace_bytes(big, 2560, 64, 4, 8, 128) <= binding.NOALLOC_SCRATCH_BYTES:
+        big *= 2
+    assert call(big) == SCRATCH
+    assert "scratch" in binding.status_str(SCRATCH)
+    assert 4096 < big  # the prefill chunk (T = 4096) fits
