@@ -69,10 +69,23 @@ def timed_calls(calls, steps, warmup, stage):
     return t1 - t0, (tot / cnt if cnt else float("nan")), cnt
 
 
-def graph_time(calls, steps, warmup):
-    """Capture len(calls) calls once into a HIP graph, replay it until `steps`
-    calls have run; returns seconds for those calls.  Inputs, outputs and the
-    workspace are preallocated, so the captured work is exactly the eager work."""
+# Every measured line replays a HIP graph at least REPLAYS times and reports
+# the median replay; a replay runs at least MIN_CALLS // REPLAYS calls (so a
+# line times at least MIN_CALLS calls whatever --steps is).
+REPLAYS = 5
+MIN_CALLS = 64
+
+
+def graph_time(calls, warmup, per_graph=None, replays=REPLAYS):
+    """Capture ``per_graph`` calls (cycling through ``calls``) into one HIP
+    graph and replay it ``replays`` times, each replay bracketed by device
+    synchronisation; returns (median seconds of one replay, per_graph).
+    Inputs, outputs and workspaces are preallocated, so the captured work is
+    exactly the eager work.  Default per_graph: a multiple of len(calls) of at
+    least MIN_CALLS / replays calls."""
+    if per_graph is None:
+        want = max(len(calls), -(-MIN_CALLS // replays))
+        per_graph = len(calls) * -(-want // len(calls))
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -80,27 +93,28 @@ def graph_time(calls, steps, warmup):
             calls[i % len(calls)]()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    per_graph = len(calls)
-    while per_graph < 16 and per_graph * 2 <= max(steps, 1):
-        per_graph *= 2
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(per_graph):
             calls[i % len(calls)]()
-    reps = max(1, steps // per_graph)
-    g.replay()
+    g.replay()  # untimed: first replay
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    times = []
+    for _ in range(replays):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         g.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
     del g
-    return t1 - t0, reps * per_graph
+    return float(np.median(times)), per_graph
 
 
-def run_single_layer(name, steps, warmup, copies, T=None):
-    """One layer of a named workload (T overrides its token count)."""
+def run_single_layer(name, steps, warmup, copies, T=None, graph_calls=None):
+    """One layer of a named workload (T overrides its token count): `steps`
+    eager calls with stage events (the expert kernel's launch time), then the
+    median of REPLAYS graph replays of `graph_calls` calls (default: at least
+    MIN_CALLS / REPLAYS)."""
     w = inputs.WORKLOADS[name]
     sh = w.shape if T is None else dataclasses.replace(w.shape, T=T)
     x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
@@ -122,7 +136,7 @@ def run_single_layer(name, steps, warmup, copies, T=None):
                                              workspace=ws)
     calls = [mk(c) for c in cps]
     secs, stage_ms, nrec = timed_calls(calls, steps, warmup, "experts")
-    gsecs, gcalls = graph_time(calls, steps, warmup)
+    gsecs, gcalls = graph_time(calls, warmup, per_graph=graph_calls)
     tokens = sh.T * steps
     return dict(shape=sh, seconds=secs, tokens=tokens, calls=steps, stage_ms=stage_ms,
                 stage_records=nrec, graph_seconds=gsecs, graph_calls=gcalls,
@@ -158,7 +172,7 @@ def run_tp_shard(name, tp, steps, warmup):
     calls = [(lambda c=c: binding.value_forward(x, c["router_w"], c["router_b"], c["expert_w"],
                                                 sh.k, sh.scale, heads, sh.head_dim, out=out,
                                                 workspace=ws)) for c in cps]
-    gsecs, gcalls = graph_time(calls, steps, warmup)
+    gsecs, gcalls = graph_time(calls, warmup)
     us = 1e6 * gsecs / gcalls
     del cps, calls
     d = {"tp": tp, "workload": name, "T": sh.T, "n_kv_heads": heads, "N": N, "weight_copies": copies,
@@ -200,7 +214,7 @@ def run_ep_shard(name, ep, steps, warmup):
                      dtype=torch.uint8, device=DEV)
     calls = [(lambda c=c: binding.value_from_routing(x, local, wts, c, sh.n_kv_heads, sh.head_dim,
                                                      out=out, workspace=ws)) for c in cps]
-    gsecs, gcalls = graph_time(calls, steps, warmup)
+    gsecs, gcalls = graph_time(calls, warmup)
     us = 1e6 * gsecs / gcalls
     del cps, calls
     d = {"ep": ep, "workload": name, "T": sh.T, "experts": e_local, "local_pairs": pairs,
@@ -235,7 +249,7 @@ def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
         return lambda: binding.value_forward_paged(x, c["router_w"], c["router_b"], c["expert_w"],
                                                    sh.k, sh.scale, pool, slots, workspace=ws)
     calls = [mk(c) for c in cps]
-    gsecs, gcalls = graph_time(calls, steps, warmup)
+    gsecs, gcalls = graph_time(calls, warmup)
     # Unfused reference: the plain forward, then a separate scatter of the
     # contiguous rows into the pool (torch index_copy_).
     out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
@@ -247,7 +261,7 @@ def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
                                   sh.n_kv_heads, sh.head_dim, out=out, workspace=ws)
             flat.index_copy_(0, slots, out.view(sh.T, sh.N))
         return f
-    usecs, ucalls = graph_time([mk2(c) for c in cps], steps, warmup)
+    usecs, ucalls = graph_time([mk2(c) for c in cps], warmup)
     return 1e6 * gsecs / gcalls, 1e6 * usecs / ucalls
 
 
@@ -270,7 +284,7 @@ def run_rebuild(name, steps, warmup, copies):
     calls = [(lambda c=c: binding.value_from_routing(x, idx, wt, c["expert_w"], sh.n_kv_heads,
                                                      sh.head_dim, out=out, workspace=ws))
              for c in cps]
-    gsecs, gcalls = graph_time(calls, steps, warmup)
+    gsecs, gcalls = graph_time(calls, warmup)
     return 1e6 * gsecs / gcalls
 
 
@@ -301,7 +315,7 @@ def run_ffn(name, steps, warmup, copies=2):
     calls = [(lambda g=g: binding.ffn_moe_forward(
         x, g["router_w"], g["router_b"], g["gate_up_w"], g["down_w"], sh.k, sh.scale,
         g["shared_gate_up_w"], g["shared_down_w"], out=out, workspace=ws)) for g in layers]
-    gsecs, gcalls = graph_time(calls, steps, warmup)
+    gsecs, gcalls = graph_time(calls, warmup)
     us = 1e6 * gsecs / gcalls
     flops = 2.0 * sh.T * (3 * sh.d * (sh.k * sh.inter + sh.inter_shared) + sh.d * sh.E)
     wbytes = 2.0 * 3 * sh.d * (touched * sh.inter + sh.inter_shared) + 2.0 * sh.E * sh.d
@@ -334,7 +348,7 @@ def run_chunked(steps, warmup):
                                       sh.scale, sh.n_kv_heads, sh.head_dim, out=outs[l][s],
                                       workspace=ws)
     secs, stage_ms, nrec = timed_calls([step], steps, warmup, "experts")
-    gsecs, gsteps = graph_time([step], steps, warmup)
+    gsecs, gsteps = graph_time([step], warmup, per_graph=2)  # 64 calls per replay
     return dict(shape=sh, seconds=secs, tokens=total * steps, layer_tokens=total * w.layers * steps,
                 calls=steps * w.chunks * w.layers, stage_ms=stage_ms, stage_records=nrec,
                 graph_seconds=gsecs, graph_calls=gsteps * w.chunks * w.layers,
@@ -360,10 +374,10 @@ def run_dense(name, steps, warmup, copies=64):
                                                      workspace=ws)) for wt in wts]
     n = max(steps, copies)
     secs, stage_ms, nrec = timed_calls(calls, n, warmup, "dense")
-    gsecs, gcalls = graph_time(calls, n, warmup)
+    gsecs, gcalls = graph_time(calls, warmup)
     out2 = torch.empty(sh.T, sh.N, dtype=torch.bfloat16, device=DEV)
     mm = [(lambda wt=wt: torch.matmul(x, wt.t(), out=out2)) for wt in wts]
-    msecs, mcalls = graph_time(mm, n, warmup)
+    msecs, mcalls = graph_time(mm, warmup)
     del wts, calls, mm
     return dict(T=sh.T, d=sh.d, N=sh.N, us=1e6 * gsecs / gcalls, kernel_us=1e3 * stage_ms,
                 launches_timed=nrec, hipblaslt_us=1e6 * msecs / mcalls)
@@ -447,31 +461,62 @@ def copy_calibration(mib, reps=5):
     log(f"copy calibration: {reps} copies of {n} bytes")
 
 
-def cpu_baseline(seconds_target=12.0):
-    """The CPU oracle on the decode workload's tokens, repeated for ~seconds_target."""
-    sys.path.insert(0, ROOT)
-    import oracle
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    w = inputs.WORKLOADS["decode"]
-    sh = w.shape
-    t = inputs.make_layer(sh, w.seed, w.dtype, w.bias)
-    o = {k: v.double().numpy() for k, v in t.items()}
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def _oracle_rate(o, sh, T, min_seconds):
+    """tokens/s of the float64 oracle on the first T tokens, repeated for at
+    least min_seconds (at least once)."""
+    import oracle
+    x = o["x"][:T]
     calls = 0
     t0 = time.perf_counter()
     while True:
-        oracle.value_forward(o["x"], o["router_w"], o["router_b"], o["expert_w"], sh.k, sh.scale,
+        oracle.value_forward(x, o["router_w"], o["router_b"], o["expert_w"], sh.k, sh.scale,
                              sh.n_kv_heads, sh.head_dim)
         calls += 1
         el = time.perf_counter() - t0
-        if el >= seconds_target:
-            break
-    return {"value": sh.T * calls / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"decode workload (T={sh.T}) evaluated {calls}x by the float64 numpy oracle, "
-                      f"{el:.1f} s, host {platform.processor() or platform.machine()}"}
+        if el >= min_seconds:
+            return T * calls / el, calls, el
+
+
+def cpu_baseline():
+    """The CPU oracle (float64 numpy, as it stands) on the host's cores:
+    * the decode workload (T=64) on every BLAS thread, ~8 s: the reported value;
+    * the prefill chunk (T=4096) on every BLAS thread, once or more (~3 s);
+    * a 512-token subset of the prefill chunk on one BLAS thread (~3 s): the
+      per-core rate."""
+    sys.path.insert(0, ROOT)
+    from threadpoolctl import threadpool_info, threadpool_limits
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    out = {}
+    for name in ("decode", "prefill"):
+        w = inputs.WORKLOADS[name]
+        t = inputs.make_layer(w.shape, w.seed, w.dtype, w.bias)
+        out[name] = (w.shape, {k: v.double().numpy() for k, v in t.items()})
+    sh, o = out["decode"]
+    dec, dcalls, dsec = _oracle_rate(o, sh, sh.T, 8.0)
+    sh, o = out["prefill"]
+    pre, pcalls, psec = _oracle_rate(o, sh, sh.T, 3.0)
+    with threadpool_limits(limits=1, user_api="blas"):
+        one, ocalls, osec = _oracle_rate(o, sh, 512, 3.0)
+    return {"value": dec, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "prefill_tokens_per_s": pre, "per_core_tokens_per_s": one,
+            "sample": f"float64 numpy oracle: decode workload (T=64) {dcalls}x in {dsec:.1f} s on "
+                      f"{threads} BLAS threads (value); prefill chunk (T=4096) {pcalls}x in "
+                      f"{psec:.1f} s on {threads} threads (prefill_tokens_per_s); its first 512 "
+                      f"tokens {ocalls}x in {osec:.1f} s on 1 thread (per_core_tokens_per_s)"}
 
 
 def main():
@@ -496,7 +541,7 @@ def main():
     torch.cuda.set_device(0)
 
     log("decode workload ...")
-    r = run_single_layer("decode", args.steps, args.warmup, args.copies)
+    r = run_single_layer("decode", args.steps, args.warmup, args.copies, graph_calls=args.steps)
     sh = r["shape"]
     step_s = r["graph_seconds"] / r["graph_calls"]
     tok_s = sh.T / step_s
@@ -521,8 +566,9 @@ def main():
                                "inputs, 4 rotated weight copies",
                    "T": sh.T, "d": sh.d, "E": sh.E, "k": sh.k, "n_kv_heads": sh.n_kv_heads,
                    "head_dim": sh.head_dim, "touched_experts": r["touched"]},
-        "timing": "steps replayed from a HIP graph of rotated-copy calls; eager "
-                  "per-call launches give eager_tokens_per_s",
+        "timing": f"median of {REPLAYS} replays of a HIP graph of exactly `steps` calls "
+                  "(rotated weight copies), each replay bracketed by device synchronisation; "
+                  "eager per-call launches give eager_tokens_per_s",
         "eager_tokens_per_s": r["tokens"] / r["seconds"],
         "max_abs_out": r["max_abs_out"],
         "whole_call": {"GB_per_s": call_bytes / step_s / 1e9,
@@ -541,7 +587,7 @@ def main():
         sec = []
         for name in ("prefill", "skewed"):
             log(f"{name} workload ...")
-            rr = run_single_layer(name, max(5, args.steps // 10), max(2, args.warmup // 4),
+            rr = run_single_layer(name, MIN_CALLS, max(2, args.warmup // 4),
                                   args.copies if name == "prefill" else 2)
             d = prefill_line(name, rr)
             d["max_over_mean_load"] = rr["max_load"] / rr["mean_load"]
@@ -549,7 +595,7 @@ def main():
             sec.append(d)
             torch.cuda.empty_cache()
         log("chunked workload ...")
-        rr = run_chunked(max(2, args.steps // 50), 1)
+        rr = run_chunked(2, 1)
         sec.append(prefill_line("chunked", rr))
         line["secondary"] = sec
         torch.cuda.empty_cache()
@@ -565,11 +611,11 @@ def main():
         line["gqa_baseline"] = gqa
         log("FFN mixture of experts ...")
         line["ffn_moe"] = [run_ffn("ffn_decode", args.steps, args.warmup),
-                           run_ffn("ffn_prefill", max(5, args.steps // 10), max(2, args.warmup // 4))]
+                           run_ffn("ffn_prefill", MIN_CALLS, max(2, args.warmup // 4))]
         torch.cuda.empty_cache()
         log("compact-cache rebuild ...")
         shp = inputs.WORKLOADS["prefill"].shape
-        rus = run_rebuild("prefill", max(5, args.steps // 10), max(2, args.warmup // 4), args.copies)
+        rus = run_rebuild("prefill", MIN_CALLS, max(2, args.warmup // 4), args.copies)
         line["compact_cache_rebuild"] = {
             "tokens": shp.T, "us": rus, "us_per_cached_token": rus / shp.T,
             "bytes_per_token_value_cache": shp.N * 2,
@@ -597,8 +643,7 @@ def main():
         for tp in (2, 8):
             shards.append(run_tp_shard("decode", tp, args.steps, args.warmup))
             torch.cuda.empty_cache()
-            shards.append(run_tp_shard("prefill", tp, max(5, args.steps // 10),
-                                       max(2, args.warmup // 4)))
+            shards.append(run_tp_shard("prefill", tp, MIN_CALLS, max(2, args.warmup // 4)))
             torch.cuda.empty_cache()
         line["tp_shard"] = shards
         log("expert-parallel shards ...")
@@ -606,8 +651,7 @@ def main():
         for ep in (2, 8):
             shards.append(run_ep_shard("decode", ep, args.steps, args.warmup))
             torch.cuda.empty_cache()
-            shards.append(run_ep_shard("prefill", ep, max(5, args.steps // 10),
-                                       max(2, args.warmup // 4)))
+            shards.append(run_ep_shard("prefill", ep, MIN_CALLS, max(2, args.warmup // 4)))
             torch.cuda.empty_cache()
         line["ep_shard"] = shards
     if not args.no_cpu_baseline:
