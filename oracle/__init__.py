@@ -13,7 +13,9 @@ Parity status per function (details in the module docstring of
   router's reduction order), ``combine_experts``, ``value_forward`` and
   ``dense_value_proj`` (the matched dense baseline) and
   ``paged_value_write`` (the paged cache store), ``rebuild_values`` (the
-  compact cache's reconstruction), ``swiglu_expert`` and ``ffn_moe_forward``
+  compact cache's reconstruction), ``pack_routing_record`` /
+  ``unpack_routing_record`` / ``rebuild_from_record`` (the compact cache's
+  record), ``swiglu_expert`` and ``ffn_moe_forward``
   (the FFN mixture of experts): pinned by the tests in
   ``tests/test_oracle_pins.py``;
 * the role of the router bias (added to the scores for selection only) and
@@ -28,7 +30,10 @@ from .mova_oracle import (  # noqa: F401
     ffn_moe_forward,
     swiglu_expert,
     paged_value_write,
+    pack_routing_record,
+    rebuild_from_record,
     rebuild_values,
+    unpack_routing_record,
     route,
     router_logits,
     sigmoid,

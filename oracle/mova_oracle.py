@@ -229,6 +229,55 @@ def rebuild_values(x, expert_w, idx, w) -> np.ndarray:
     return out
 
 
+# Bits per expert id in the compact routing record (E <= 64 experts).
+RECORD_ID_BITS = 6
+# Slots one 32-bit id word holds.
+RECORD_MAX_K = 32 // RECORD_ID_BITS
+
+
+def pack_routing_record(idx, w):
+    """Compact routing record of a token (Option B of the page "IFM K2 Horizon
+    Deep Dive: Inside Mixture-of-Value Attention (MoVA) ...", section "The Two
+    Architectural Caching Strategies for MoVA": the cache keeps x_t together
+    with the top-4 expert ids and four fp16 weights).
+
+    Reading (the page's "16-bit mask" cannot hold four ids out of 64): the k
+    ids of a token are packed at RECORD_ID_BITS bits each into one unsigned
+    32-bit word, slot j in bits [6j, 6j + 6), so k <= 5; the k weights are
+    rounded to fp16 (IEEE binary16, nearest even).  At k = 4 a record is
+    4 + 8 = 12 bytes per token.
+
+    idx [T, k] integers in [0, 64), w [T, k] -> (ids [T] uint32, w16 [T, k] float16).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    if k > RECORD_MAX_K:
+        raise ValueError(f"a record holds at most {RECORD_MAX_K} slots")
+    if (idx < 0).any() or (idx >= (1 << RECORD_ID_BITS)).any():
+        raise ValueError("expert ids must lie in [0, 64)")
+    ids = np.zeros(T, dtype=np.uint64)
+    for j in range(k):
+        ids += idx[:, j].astype(np.uint64) << np.uint64(RECORD_ID_BITS * j)
+    w16 = _f64(w).reshape(T, k).astype(np.float16)  # one rounding, nearest even
+    return ids.astype(np.uint32), w16
+
+
+def unpack_routing_record(ids, w16, k: int):
+    """The inverse of ``pack_routing_record``: (idx [T, k] int64, w [T, k]
+    float64 holding the fp16 values exactly)."""
+    ids = np.asarray(ids, dtype=np.uint64)
+    mask = np.uint64((1 << RECORD_ID_BITS) - 1)
+    idx = np.stack([(ids >> np.uint64(RECORD_ID_BITS * j)) & mask for j in range(k)], axis=1)
+    return idx.astype(np.int64), np.asarray(w16, dtype=np.float16).astype(np.float64).reshape(-1, k)
+
+
+def rebuild_from_record(x, expert_w, ids, w16, k: int) -> np.ndarray:
+    """Value vectors rebuilt from stored x_t and a stored compact record: the
+    record unpacked, then ``rebuild_values`` (ids >= E mark unused slots)."""
+    idx, w = unpack_routing_record(ids, w16, k)
+    return rebuild_values(x, expert_w, idx, w)
+
+
 def swiglu_expert(x, gate_w, up_w, down_w) -> np.ndarray:
     """One SwiGLU FFN expert, down( SiLU(gate x) * (up x) ), bias-free,
     nn.Linear weight layout ([out, in]).  Rows of x are tokens."""
