@@ -266,26 +266,37 @@ def run_paged_decode(steps, warmup, copies, block_size=16, num_blocks=4096):
 
 
 def run_rebuild(name, steps, warmup, copies):
-    """Values of the workload's tokens rebuilt from their stored routing
-    (mova_value_from_routing), as a compact cache that keeps x_t and the
-    routing instead of v_t would have to at attention time."""
+    """Values of the workload's tokens rebuilt from stored x_t and their
+    compact routing records (mova_value_from_record), as a compact cache that
+    keeps x_t and the record instead of v_t would have to at attention time;
+    also the forward that writes the records (mova_value_forward_record)
+    against the plain forward.  Returns (rebuild us, record-writing forward
+    us, plain forward us)."""
     w = inputs.WORKLOADS[name]
     sh = w.shape
     x = inputs.make_tokens(sh.T, sh.d, w.seed, w.dtype).to(DEV)
     cps = make_copies(sh, w.seed, w.dtype, w.bias, copies)
-    idx = torch.empty(sh.T, sh.k, dtype=torch.int32, device=DEV)
-    wt = torch.empty(sh.T, sh.k, dtype=torch.float32, device=DEV)
-    binding.value_forward(x, cps[0]["router_w"], cps[0]["router_b"], cps[0]["expert_w"], sh.k,
-                          sh.scale, sh.n_kv_heads, sh.head_dim, topk_idx=idx, topk_w=wt)
-    wt = wt.half().float()  # the compact record keeps fp16 weights
     out = torch.empty(sh.T, sh.n_kv_heads, sh.head_dim, dtype=torch.bfloat16, device=DEV)
+    ids = torch.empty(sh.T, dtype=torch.int32, device=DEV)
+    w16 = torch.empty(sh.T, sh.k, dtype=torch.float16, device=DEV)
     ws = torch.empty(binding.workspace_bytes(sh.T, sh.d, sh.E, sh.k, sh.n_kv_heads, sh.head_dim),
                      dtype=torch.uint8, device=DEV)
-    calls = [(lambda c=c: binding.value_from_routing(x, idx, wt, c["expert_w"], sh.n_kv_heads,
-                                                     sh.head_dim, out=out, workspace=ws))
+    binding.value_forward_record(x, cps[0]["router_w"], cps[0]["router_b"], cps[0]["expert_w"],
+                                 sh.k, sh.scale, sh.n_kv_heads, sh.head_dim, out=out,
+                                 record_ids=ids, record_w=w16, workspace=ws)
+    calls = [(lambda c=c: binding.value_from_record(x, ids, w16, c["expert_w"], sh.n_kv_heads,
+                                                    sh.head_dim, out=out, workspace=ws))
              for c in cps]
     gsecs, gcalls = graph_time(calls, warmup)
-    return 1e6 * gsecs / gcalls
+    rec = [(lambda c=c: binding.value_forward_record(
+        x, c["router_w"], c["router_b"], c["expert_w"], sh.k, sh.scale, sh.n_kv_heads, sh.head_dim,
+        out=out, record_ids=ids, record_w=w16, workspace=ws)) for c in cps]
+    rsecs, rcalls = graph_time(rec, warmup)
+    plain = [(lambda c=c: binding.value_forward(
+        x, c["router_w"], c["router_b"], c["expert_w"], sh.k, sh.scale, sh.n_kv_heads, sh.head_dim,
+        out=out, workspace=ws)) for c in cps]
+    psecs, pcalls = graph_time(plain, warmup)
+    return 1e6 * gsecs / gcalls, 1e6 * rsecs / rcalls, 1e6 * psecs / pcalls
 
 
 def run_ffn(name, steps, warmup, copies=2):
@@ -615,13 +626,17 @@ def main():
         torch.cuda.empty_cache()
         log("compact-cache rebuild ...")
         shp = inputs.WORKLOADS["prefill"].shape
-        rus = run_rebuild("prefill", MIN_CALLS, max(2, args.warmup // 4), args.copies)
+        rus, rec_us, plain_us = run_rebuild("prefill", MIN_CALLS, max(2, args.warmup // 4),
+                                            args.copies)
         line["compact_cache_rebuild"] = {
             "tokens": shp.T, "us": rus, "us_per_cached_token": rus / shp.T,
+            "forward_with_records_us": rec_us, "forward_us": plain_us,
             "bytes_per_token_value_cache": shp.N * 2,
+            "bytes_per_token_record": 4 + 2 * shp.k,
             "bytes_per_token_compact": shp.d * 2 + 4 + 2 * shp.k,
-            "note": "values of 4096 cached tokens rebuilt from stored x_t, top-4 ids and fp16 "
-                    "weights (no router); a value cache reads the 2 KiB rows instead"}
+            "note": "values of 4096 cached tokens rebuilt from stored x_t and their compact "
+                    "routing records (6-bit ids in one 32-bit word, fp16 weights; no router); a "
+                    "value cache reads the 2 KiB rows instead"}
         log("paged decode ...")
         pus, uus = run_paged_decode(args.steps, args.warmup, args.copies)
         line["paged_decode"] = {"us_per_step": pus, "plain_us_per_step": 1e6 * step_s,

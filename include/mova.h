@@ -205,6 +205,54 @@ int mova_value_forward_noalloc(const void* x, const void* router_w, const float*
                                int32_t* topk_idx_out, float* topk_w_out, hipStream_t stream);
 
 /*
+ * Compact routing record of the compact value cache (page "IFM K2 Horizon
+ * Deep Dive: Inside Mixture-of-Value Attention (MoVA) ...", section "The Two
+ * Architectural Caching Strategies for MoVA", Option B, which keeps a token's
+ * x_t with its top-4 expert ids and four fp16 weights and rebuilds v_t from
+ * them).  Layout, per token t:
+ *
+ *   record_ids uint32 [T]     slot j's expert id in bits [6j, 6j + 6), j < k
+ *                             (k <= 5; E <= 64 ids fit 6 bits); higher bits 0
+ *   record_w   fp16   [T, k]  slot j's routing weight, IEEE binary16, rounded
+ *                             to nearest even from the fp32 weight
+ *
+ * 4 + 2k bytes per token (12 at k = 4), stored beside the token's x_t.  The
+ * page's "16-bit mask" cannot hold four ids out of 64, so the ids take one
+ * 32-bit word.  record_ids must be 4-byte aligned, record_w 2-byte aligned.
+ */
+
+/*
+ * mova_value_forward that also writes each token's compact routing record
+ * (the routing the call used, packed as above).  Same arguments, workspace,
+ * numerics and outputs as mova_value_forward otherwise.  k > 5 returns
+ * MOVA_ERR_UNSUPPORTED; a NULL or misaligned record pointer (T > 0) returns
+ * MOVA_ERR_INVALID_ARG, before anything is enqueued.
+ */
+int mova_value_forward_record(const void* x, const void* router_w, const float* router_b,
+                              const void* expert_w, int T, int d, int E, int k, float scale,
+                              int n_kv_heads, int head_dim, void* out, uint32_t* record_ids,
+                              void* record_w, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * Value vectors rebuilt from stored x_t and stored compact records: the
+ * records unpacked (ids, fp16 weights widened exactly to fp32), then exactly
+ * mova_value_from_routing -- the same kernels, the same bits as
+ * mova_value_from_routing given the unpacked routing.  An id >= E (possible
+ * only when E < 64) marks an unused slot; so does a zero weight.
+ *
+ *   x          bf16 [T, d]; record_ids, record_w as above; expert_w, out,
+ *   workspace (mova_workspace_bytes) as for mova_value_forward.
+ *
+ * k > 5 returns MOVA_ERR_UNSUPPORTED; otherwise errors as for
+ * mova_value_from_routing.
+ */
+int mova_value_from_record(const void* x, const uint32_t* record_ids, const void* record_w,
+                           const void* expert_w, int T, int d, int E, int k, int n_kv_heads,
+                           int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Bytes of device workspace mova_dense_value_proj needs for these sizes: 0
  * when T == 0 or T > 256, (size_t)-1 outside the supported domain (that of
  * mova_value_forward without the router's E and k).

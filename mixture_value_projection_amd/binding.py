@@ -52,6 +52,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                              vp, vp, vp, sz, vp]
     lib.mova_value_forward_noalloc.restype = i
     lib.mova_value_forward_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, vp, vp]
+    lib.mova_value_forward_record.restype = i
+    lib.mova_value_forward_record.argtypes = [vp, vp, vp, vp, i, i, i, i, f, i, i, vp, vp, vp, vp,
+                                              sz, vp]
+    lib.mova_value_from_record.restype = i
+    lib.mova_value_from_record.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, sz, vp]
     lib.mova_value_from_routing.restype = i
     lib.mova_value_from_routing.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, sz, vp]
     lib.mova_ffn_workspace_bytes.restype = sz
@@ -299,6 +304,87 @@ def value_from_routing(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Te
                                      workspace.numel(), _stream(dev))
     if rc != MOVA_OK:
         raise MovaError(rc, "mova_value_from_routing")
+    return out
+
+
+def value_forward_record(x: torch.Tensor, router_w: torch.Tensor,
+                         router_b: Optional[torch.Tensor], expert_w: torch.Tensor, k: int,
+                         scale: float = 2.5, n_kv_heads: Optional[int] = None, head_dim: int = 128,
+                         out: Optional[torch.Tensor] = None,
+                         record_ids: Optional[torch.Tensor] = None,
+                         record_w: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """mova_value_forward_record: returns (out bf16 [T, H, D], record_ids int32
+    [T] holding the uint32 words, record_w float16 [T, k])."""
+    lib = load_library()
+    T, d = x.shape
+    E, N, d2 = expert_w.shape
+    if d2 != d:
+        raise ValueError("expert_w's last dim must equal x's width")
+    if n_kv_heads is None:
+        n_kv_heads = N // head_dim
+    if n_kv_heads * head_dim != N:
+        raise ValueError("n_kv_heads * head_dim must equal the expert width")
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(router_w, "router_w", torch.bfloat16, (E, d), dev)
+    if router_b is not None:
+        _check(router_b, "router_b", torch.float32, (E,), dev)
+    _check(expert_w, "expert_w", torch.bfloat16, (E, N, d), dev)
+    if out is None:
+        out = torch.empty(T, n_kv_heads, head_dim, dtype=torch.bfloat16, device=dev)
+    if record_ids is None:
+        record_ids = torch.empty(T, dtype=torch.int32, device=dev)
+    if record_w is None:
+        record_w = torch.empty(T, k, dtype=torch.float16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, n_kv_heads, head_dim), dev)
+    _check(record_ids, "record_ids", torch.int32, (T,), dev)
+    _check(record_w, "record_w", torch.float16, (T, k), dev)
+    nbytes = workspace_bytes(T, d, E, k, n_kv_heads, head_dim)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = lib.mova_value_forward_record(_ptr(x), _ptr(router_w), _ptr(router_b), _ptr(expert_w),
+                                       T, d, E, k, float(scale), n_kv_heads, head_dim, _ptr(out),
+                                       _ptr(record_ids), _ptr(record_w), _ptr(workspace),
+                                       workspace.numel(), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_value_forward_record")
+    return out, record_ids, record_w
+
+
+def value_from_record(x: torch.Tensor, record_ids: torch.Tensor, record_w: torch.Tensor,
+                      expert_w: torch.Tensor, n_kv_heads: Optional[int] = None,
+                      head_dim: int = 128, out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """mova_value_from_record: value vectors rebuilt from stored inputs and
+    compact records (record_ids int32 [T] as uint32 words, record_w float16
+    [T, k])."""
+    lib = load_library()
+    T, d = x.shape
+    E, N, d2 = expert_w.shape
+    k = record_w.shape[1] if record_w.dim() == 2 else -1
+    if d2 != d:
+        raise ValueError("expert_w's last dim must equal x's width")
+    if n_kv_heads is None:
+        n_kv_heads = N // head_dim
+    if n_kv_heads * head_dim != N:
+        raise ValueError("n_kv_heads * head_dim must equal the expert width")
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (T, d), dev)
+    _check(record_ids, "record_ids", torch.int32, (T,), dev)
+    _check(record_w, "record_w", torch.float16, (T, k), dev)
+    _check(expert_w, "expert_w", torch.bfloat16, (E, N, d), dev)
+    if out is None:
+        out = torch.empty(T, n_kv_heads, head_dim, dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, (T, n_kv_heads, head_dim), dev)
+    nbytes = workspace_bytes(T, d, E, k, n_kv_heads, head_dim)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = lib.mova_value_from_record(_ptr(x), _ptr(record_ids), _ptr(record_w), _ptr(expert_w), T, d,
+                                    E, k, n_kv_heads, head_dim, _ptr(out), _ptr(workspace),
+                                    workspace.numel(), _stream(dev))
+    if rc != MOVA_OK:
+        raise MovaError(rc, "mova_value_from_record")
     return out
 
 

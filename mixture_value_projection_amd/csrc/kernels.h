@@ -182,6 +182,15 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
+// Compact routing record (record.hip): k ids at kRecordIdBits bits each in
+// one 32-bit word per token (k <= kRecordMaxK), k fp16 weights.
+constexpr int kRecordIdBits = 6;
+constexpr int kRecordMaxK = 32 / kRecordIdBits;
+hipError_t launch_record_pack(const int32_t* idx, const float* w, int T, int k, uint32_t* ids,
+                              f16_t* w16, hipStream_t stream);
+hipError_t launch_record_unpack(const uint32_t* ids, const f16_t* w16, int T, int k, int32_t* idx,
+                                float* w, hipStream_t stream);
+
 // FFN mixture of experts (ffn.hip): router for E <= kMaxDispatchExperts
 // (partial logits in plog, ffn_router_plog_floats(T) floats; selection in
 // workgroups of ffn_router_chunk_tokens() tokens, which is also the dispatch

@@ -512,6 +512,63 @@ int mova_value_from_routing(const void* x, const int32_t* topk_idx, const float*
                             &given);
 }
 
+int mova_value_forward_record(const void* x, const void* router_w, const float* router_b,
+                              const void* expert_w, int T, int d, int E, int k, float scale,
+                              int n_kv_heads, int head_dim, void* out, uint32_t* record_ids,
+                              void* record_w, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  int rc = check_shape(T, d, E, k);
+  if (rc != MOVA_OK) return rc;
+  if (k > kRecordMaxK) return MOVA_ERR_UNSUPPORTED;
+  rc = check_heads(n_kv_heads, head_dim);
+  if (rc != MOVA_OK) return rc;
+  if (T > 0 && (record_ids == nullptr || record_w == nullptr)) return MOVA_ERR_INVALID_ARG;
+  if (((uintptr_t)record_ids & 3u) != 0 || ((uintptr_t)record_w & 1u) != 0)
+    return MOVA_ERR_INVALID_ARG;
+  rc = value_forward_impl(x, router_w, router_b, expert_w, T, d, E, k, scale, n_kv_heads, head_dim,
+                          out, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+  if (rc != MOVA_OK || T == 0) return rc;
+  // The routing the call used sits in the workspace (no routing outputs were
+  // requested); pack it.
+  const Layout L = layout(T, E, k, n_kv_heads * head_dim);
+  char* ws = (char*)workspace;
+  return launch_record_pack((const int32_t*)(ws + L.idx), (const float*)(ws + L.w), T, k,
+                            record_ids, (f16_t*)record_w, stream) == hipSuccess
+             ? MOVA_OK
+             : MOVA_ERR_HIP;
+}
+
+int mova_value_from_record(const void* x, const uint32_t* record_ids, const void* record_w,
+                           const void* expert_w, int T, int d, int E, int k, int n_kv_heads,
+                           int head_dim, void* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  int rc = check_shape(T, d, E, k);
+  if (rc != MOVA_OK) return rc;
+  if (k > kRecordMaxK) return MOVA_ERR_UNSUPPORTED;
+  rc = check_heads(n_kv_heads, head_dim);
+  if (rc != MOVA_OK) return rc;
+  if (T == 0) return MOVA_OK;
+  if (record_ids == nullptr || record_w == nullptr) return MOVA_ERR_INVALID_ARG;
+  if (((uintptr_t)record_ids & 3u) != 0 || ((uintptr_t)record_w & 1u) != 0)
+    return MOVA_ERR_INVALID_ARG;
+  const Layout L = layout(T, E, k, n_kv_heads * head_dim);
+  if (workspace == nullptr || workspace_bytes < L.total) return MOVA_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return MOVA_ERR_INVALID_ARG;
+  if (x == nullptr || expert_w == nullptr || out == nullptr) return MOVA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(expert_w) || !aligned16(out)) return MOVA_ERR_INVALID_ARG;
+  // Unpack into the workspace's routing regions (unused when the routing is
+  // given), then rebuild as mova_value_from_routing does.
+  char* ws = (char*)workspace;
+  int32_t* idx = (int32_t*)(ws + L.idx);
+  float* w = (float*)(ws + L.w);
+  if (launch_record_unpack(record_ids, (const f16_t*)record_w, T, k, idx, w, stream) != hipSuccess)
+    return MOVA_ERR_HIP;
+  const GivenRouting given{idx, w};
+  return value_forward_impl(x, nullptr, nullptr, expert_w, T, d, E, k, 1.0f, n_kv_heads, head_dim,
+                            out, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+                            &given);
+}
+
 int mova_value_forward_paged(const void* x, const void* router_w, const float* router_b,
                              const void* expert_w, int T, int d, int E, int k, float scale,
                              int n_kv_heads, int head_dim, void* v_cache, int num_blocks,

@@ -320,3 +320,20 @@ def test_noalloc_rejects_before_touching_the_gpu(lib):
     assert call(big) == SCRATCH
     assert "scratch" in binding.status_str(SCRATCH)
     assert 4096 < big  # the prefill chunk (T = 4096) fits
+
+
+def test_record_entry_points_reject_on_the_host(lib):
+    """mova_value_forward_record / mova_value_from_record: shape and pointer
+    errors are refused before anything is enqueued."""
+    def fwd_rec(T=16, k=2, ids=FAKE, w=FAKE):
+        return lib.mova_value_forward_record(FAKE, FAKE, None, FAKE, T, 256, 8, k, 2.5, 2, 32, FAKE,
+                                             ids, w, FAKE, 1 << 30, None)
+
+    def from_rec(T=16, k=2, ids=FAKE, w=FAKE, ws=FAKE):
+        return lib.mova_value_from_record(FAKE, ids, w, FAKE, T, 256, 8, k, 2, 32, FAKE, ws, 1 << 30,
+                                          None)
+    assert fwd_rec(T=0) == OK and from_rec(T=0) == OK
+    assert fwd_rec(k=6) == UNSUPPORTED and from_rec(k=6) == UNSUPPORTED
+    assert fwd_rec(ids=None) == INVALID and from_rec(w=None) == INVALID
+    assert fwd_rec(ids=FAKE + 2) == INVALID and from_rec(w=FAKE + 1) == INVALID
+    assert from_rec(ws=None) == WORKSPACE
