@@ -104,7 +104,10 @@ int mova_route(const void* x, const void* router_w, const float* router_b,
  * Expert products accumulate in fp32; SiLU and the routing weight are applied
  * in fp32 and each slot's result is kept as fp16 (rounded to nearest even);
  * the k-way sum is fp32 in a fixed slot order (i = 0..k-1), rounded once to
- * bf16 (nearest even).  Results are bitwise reproducible for identical inputs and do not
+ * bf16 (nearest even).  Range: the fp16 slot value holds |w * SiLU(z)| up to
+ * 65504 (the largest finite fp16); a slot beyond it becomes +-inf, and so does
+ * its token's output row element, although the sum itself would fit bf16.
+ * The value layer's own scales stay far below (|out| < 8 on the workloads).  Results are bitwise reproducible for identical inputs and do not
  * depend on how the tokens are split across calls.
  */
 int mova_value_forward(const void* x, const void* router_w, const float* router_b,
