@@ -369,7 +369,8 @@ int mova_ffn_moe_forward(const void* x, const void* router_w, const float* route
  */
 enum mova_override {
   MOVA_OVERRIDE_PATH = 0,          /* 1: decode kernel (T <= 256), 2: dispatch + grouped GEMM */
-  MOVA_OVERRIDE_ROUTER = 1,        /* 1: tile router, 2 / 3: staged router, 32 / 64 tokens */
+  MOVA_OVERRIDE_ROUTER = 1,        /* tokens per router workgroup: 1: 16, 2: 32 (4 LDS
+                                      stages), 3: 32 (3 stages), 4: 64 */
   MOVA_OVERRIDE_GEMM_TILE = 2,     /* 1: 256x256, 2: 128x256, 3: 128x128, 4: 128x128 with 3
                                       stages, 5: with 4 stages, 6: 128x128 on 4 waves,
                                       7: 352x256 (routed GEMMs only) */

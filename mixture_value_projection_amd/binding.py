@@ -499,7 +499,7 @@ def dense_value_proj(x: torch.Tensor, w_v: torch.Tensor, n_kv_heads: Optional[in
 # Kernel-choice overrides (mova_debug_override): name -> (key, {value name: value}).
 OVERRIDES = {
     "path": (0, {"decode": 1, "grouped": 2}),
-    "router": (1, {"tile": 1, "staged32": 2, "staged64": 3}),
+    "router": (1, {"16": 1, "32s4": 2, "32s3": 3, "64": 4}),
     "gemm_tile": (2, {"256x256": 1, "128x256": 2, "128x128": 3, "128x128s3": 4,
                       "128x128s4": 5, "128x128w4": 6, "352x256": 7}),
     "dense_path": (3, {"skinny": 1, "tiled": 2}),

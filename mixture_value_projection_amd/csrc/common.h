@@ -51,4 +51,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// ---- direct-to-LDS staging (global_load_lds rings) --------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate: at most n vector-memory operations of this wave still
+// outstanding, and all of its LDS operations complete.
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// waits for every outstanding direct-to-LDS load, which would drain a
+// multi-stage ring.  The caller waits on the counters it needs first; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void raw_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace mova

@@ -52,13 +52,13 @@ struct RouterArgs {
   int32_t* chunk_counts;  // [blocks, E] or null
 };
 
-// Tile router: one workgroup per router_tile_tokens(T) tokens, top-k fused;
-// with chunk_counts set, each workgroup writes its per-expert pair counts
-// ([blocks, E]), so the dispatch chunk is router_tile_tokens(T) tokens.
-int router_tile_tokens(int T);
-hipError_t launch_router_tile(const RouterArgs& a, hipStream_t stream);
+// LDS-staged router: one workgroup per router_chunk_tokens(T) tokens, top-k
+// fused; with chunk_counts set, each workgroup writes its per-expert pair
+// counts ([blocks, E]), so the dispatch chunk is router_chunk_tokens(T) tokens.
+int router_chunk_tokens(int T);
+hipError_t launch_router_lds(const RouterArgs& a, hipStream_t stream);
 // Small-T router: partial logits over many single-wave blocks, then top-k.
-// Same bits as launch_router_tile.  plog: router_small_plog_floats(T) floats.
+// Same bits as launch_router_lds.  plog: router_small_plog_floats(T) floats.
 int router_small_plog_floats(int T);
 hipError_t launch_router_small(const RouterArgs& a, float* plog, hipStream_t stream);
 

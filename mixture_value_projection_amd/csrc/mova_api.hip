@@ -45,7 +45,7 @@ enum class Path { Decode, Grouped };
 
 // Kernel-choice overrides (mova_debug_override); largest value per key.
 std::atomic<int> g_override[kOvCount];
-constexpr int kOverrideMax[kOvCount] = {2, 3, 7, 2, 2, 2, 1};
+constexpr int kOverrideMax[kOvCount] = {2, 4, 7, 2, 2, 2, 1};
 
 // Path forced by the kOvPath override: 1 the decode kernel (where T allows
 // it), 2 dispatch and the grouped GEMM; 0 when none applies.
@@ -386,10 +386,9 @@ int mova_route(const void* x, const void* router_w, const float* router_b, int T
     return MOVA_ERR_INVALID_ARG;
   RouterArgs ra{(const __bf16*)x, (const __bf16*)router_w, router_b, T, d, E, k, scale,
                 topk_idx, topk_w, nullptr};
-  // Routing alone has no workspace, so it uses the single-kernel routers
-  // (tile or staged by T; same bits as the two-kernel small-T router of the
-  // decode path).
-  return launch_router_tile(ra, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+  // Routing alone has no workspace, so it uses the single-kernel router at
+  // every T (same bits as the two-kernel small-T router of the decode path).
+  return launch_router_lds(ra, stream) == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
 }
 
 // Shared body of mova_value_forward, mova_value_forward_paged and
@@ -453,7 +452,7 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w,
                   grouped ? chunk : nullptr};
-    err = grouped ? launch_router_tile(ra, stream) : launch_router_small(ra, plog, stream);
+    err = grouped ? launch_router_lds(ra, stream) : launch_router_small(ra, plog, stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
 
@@ -465,7 +464,7 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
     const GemmTile tile = gemm_tile_grouped(T, k, E, N);
     {
       StageScope sc(1, stream);
-      DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, router_tile_tokens(T), tile.bm};
+      DispatchArgs dp{idx, chunk, eoff, tbase, perm, T, E, k, router_chunk_tokens(T), tile.bm};
       if (given != nullptr) err = launch_dispatch_count(dp, stream);
       if (err == hipSuccess) err = launch_dispatch(dp, stream);
     }

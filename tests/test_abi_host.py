@@ -75,7 +75,7 @@ def test_workspace_bytes_independent_of_kernel_choice(T):
     """The workspace size depends on the shapes alone, not on which router or
     expert kernel a call will take (the switches that force them)."""
     want = binding.workspace_bytes(T, 2560, 64, 4, 8, 128)
-    for name, val in [("router", "tile"), ("router", "staged32"), ("router", "staged64"),
+    for name, val in [("router", "16"), ("router", "32s4"), ("router", "32s3"), ("router", "64"),
                       ("path", "grouped"), ("path", "decode"), ("gemm_tile", "128x128")]:
         with binding.overrides(**{name: val}):
             assert binding.workspace_bytes(T, 2560, 64, 4, 8, 128) == want, (name, val)

@@ -149,19 +149,22 @@ def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode):
 
 
 
-@pytest.mark.parametrize("T,d,E,k", [(4096, 2560, 64, 4), (1000, 320, 40, 8), (777, 192, 7, 3),
-                                     (8192, 2560, 64, 4), (33, 2560, 64, 6)])
-def test_staged_router_bitwise(T, d, E, k):
-    """The staged-weight router (32- or 64-token workgroups, the weight shared
-    through LDS) gives the tile router's routing bits, and the grouped path
-    built on its dispatch chunks gives the same output bits."""
-    shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=1, head_dim=64)
-    g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, T + d, torch.bfloat16, "uniform").items()}
+@pytest.mark.parametrize("T,d,E,k,mode", [(4096, 2560, 64, 4, "uniform"), (1000, 320, 40, 8, "uniform"),
+                                          (777, 192, 7, 3, "uniform"), (8192, 2560, 64, 4, "uniform"),
+                                          (33, 2560, 64, 6, "uniform"), (1000, 512, 64, 4, "ties"),
+                                          (600, 2560, 64, 8, "one_expert")])
+def test_router_configs_bitwise(T, d, E, k, mode):
+    """Every router configuration (16, 32 or 64 tokens per workgroup; 2 to 4
+    LDS stages) gives the same routing bits, and the grouped path built on its
+    dispatch chunks the same output bits, also with tied scores and with every
+    token on one expert."""
+    g = _layer(T, d, E, k, 1, 64, seed=T + d, mode=mode)
     binding.set_override("path", "grouped")
     res = {}
-    for kind in ("tile", "staged32", "staged64"):
+    kinds = ("16", "32s4", "32s3", "64")
+    for kind in kinds:
         binding.set_override("router", kind)
-        print(f"router {kind} T={T} d={d} E={E} k={k}", flush=True)
+        print(f"router {kind} T={T} d={d} E={E} k={k} {mode}", flush=True)
         idx, w = binding.route(g["x"], g["router_w"], g["router_b"], k, 2.5)
         out = binding.value_forward(g["x"], g["router_w"], g["router_b"], g["expert_w"], k, 2.5,
                                     1, 64)
@@ -169,9 +172,14 @@ def test_staged_router_bitwise(T, d, E, k):
         res[kind] = (idx, w, out)
     binding.set_override("router", None)
     binding.set_override("path", None)
-    for kind in ("staged32", "staged64"):
-        for name, a, b in zip(("idx", "w", "out"), res[kind], res["tile"]):
-            assert torch.equal(a, b), f"{kind}: {name} differs from the tile router"
+    for kind in kinds[1:]:
+        for name, a, b in zip(("idx", "w", "out"), res[kind], res["16"]):
+            assert torch.equal(a, b), f"{kind}: {name} differs from the 16-token router"
+    if mode == "ties":
+        for row in res["16"][0].cpu().tolist():
+            for pos, e in enumerate(row):
+                if e % 2 == 1:
+                    assert e - 1 in row[:pos], f"tie order broken in {row}"
 
 
 @pytest.mark.parametrize("groups", ["1", "2"])
