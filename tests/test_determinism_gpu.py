@@ -128,7 +128,7 @@ def _run(g, k, heads, hd, forced):
 ])
 def test_decode_and_grouped_paths_bitwise(T, d, E, k, heads, hd, mode):
     """The decode path (two-kernel router, weight-streaming experts) and the
-    grouped path (tile router, dispatch, grouped GEMM) give the same routing,
+    grouped path (LDS-staged router, dispatch, grouped GEMM) give the same routing,
     weights and output bits, also with tied scores and with every token on
     one expert."""
     g = _layer(T, d, E, k, heads, hd, seed=T + E, mode=mode)
