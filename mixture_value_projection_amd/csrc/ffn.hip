@@ -197,7 +197,13 @@ __global__ __launch_bounds__(kTopkThreads) void ffn_topk_kernel(const float* __r
   if (counts != nullptr && tid < E) counts[(size_t)blockIdx.x * E + tid] = hist[tid];
 }
 
+// Above kFfnLdsMinT tokens the LDS-staged router (router.hip) takes the call:
+// the same chains, selection order and weights, hence the same bits, with its
+// operands loaded as whole row segments instead of MFMA fragments.
+constexpr int kFfnLdsMinT = 1024;
+
 hipError_t launch_ffn_router(const RouterArgs& a, float* plog, hipStream_t stream) {
+  if (a.T >= kFfnLdsMinT) return launch_router_lds_wide(a, stream);
   const int tb = ceil_div(a.T, kFfnTokens);
   const int tiles = ceil_div(a.E, 16);
   if (a.T >= 1024)

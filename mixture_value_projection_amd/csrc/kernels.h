@@ -57,6 +57,9 @@ struct RouterArgs {
 // counts ([blocks, E]), so the dispatch chunk is router_chunk_tokens(T) tokens.
 int router_chunk_tokens(int T);
 hipError_t launch_router_lds(const RouterArgs& a, hipStream_t stream);
+// The same kernel for up to 128 experts, 16 tokens per workgroup (the FFN
+// router's chunk), no override.
+hipError_t launch_router_lds_wide(const RouterArgs& a, hipStream_t stream);
 // Small-T router: partial logits over many single-wave blocks, then top-k.
 // Same bits as launch_router_lds.  plog: router_small_plog_floats(T) floats.
 int router_small_plog_floats(int T);

@@ -102,6 +102,67 @@ __device__ __forceinline__ void topk_tokens(const float (&logit)[NT], float b_la
   }
 }
 
+// topk_tokens for up to 128 experts, two per lane: lane l holds experts l
+// (logit0) and l + 64 (logit1).  Each round takes the wave-wide maximum of
+// the lanes' larger key; the winner is the lowest expert index among the
+// keys equal to it (experts 0 .. 63 first, then 64 .. 127).  Same selection
+// order, weight sum and weights as topk_tokens.
+template <int NT>
+__device__ __forceinline__ void topk_tokens2(const float (&logit0)[NT], const float (&logit1)[NT],
+                                             float b0, float b1, int lane, int E, int k,
+                                             float scale, int (&my_idx)[NT], float (&my_w)[NT]) {
+  float sc0[NT], sc1[NT], ssum[NT], mine[NT];
+  uint32_t key0[NT], key1[NT];
+  int pick[NT];
+  auto order = [](float sel) {
+    sel = (sel == 0.f) ? 0.f : sel;  // -0 and +0 rank as equal, as in a float compare
+    const uint32_t u = __float_as_uint(sel);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  };
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    sc0[i] = sigmoidf_fast(logit0[i]);
+    sc1[i] = sigmoidf_fast(logit1[i]);
+    key0[i] = lane < E ? order(sc0[i] + b0) : 0u;
+    key1[i] = lane + 64 < E ? order(sc1[i] + b1) : 0u;
+    ssum[i] = 0.f;
+    mine[i] = 0.f;
+    pick[i] = 0;
+  }
+  for (int r = 0; r < k; ++r) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      uint32_t m = key0[i] > key1[i] ? key0[i] : key1[i];
+      m = max_dpp<0x121, 0xF>(m);
+      m = max_dpp<0x122, 0xF>(m);
+      m = max_dpp<0x124, 0xF>(m);
+      m = max_dpp<0x128, 0xF>(m);
+      m = max_dpp<0x142, 0xA>(m);
+      m = max_dpp<0x143, 0xC>(m);
+      const uint32_t top = (uint32_t)__builtin_amdgcn_readlane((int)m, 63);
+      const uint64_t hits0 = __ballot(key0[i] == top);
+      const uint64_t hits1 = __ballot(key1[i] == top);
+      const int win = __builtin_amdgcn_readfirstlane(
+          hits0 != 0ull ? __ffsll((unsigned long long)hits0) - 1
+                        : 64 + __ffsll((unsigned long long)hits1) - 1);
+      const float sv = win < 64 ? sc0[i] : sc1[i];  // win is wave-uniform
+      const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv), win & 63));
+      ssum[i] += ws;
+      if (lane == r) {
+        pick[i] = win;
+        mine[i] = ws;
+      }
+      if (lane == win) key0[i] = 0u;
+      if (lane + 64 == win) key1[i] = 0u;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    my_idx[i] = min(max(pick[i], 0), E - 1);
+    my_w[i] = scale * mine[i] / ssum[i];
+  }
+}
+
 // ---- LDS-staged router: one workgroup of 4 waves per TM = 16 * TG tokens ----
 //
 // A fragment load straight from memory (lane = row % 16, 16 B of k per lane)
@@ -120,21 +181,23 @@ __device__ __forceinline__ void topk_tokens(const float (&logit)[NT], float b_la
 // expert, TM / 4 tokens per wave (topk_tokens).  A workgroup's tokens form
 // one dispatch chunk: with chunk_counts given, it receives the workgroup's
 // per-expert pair counts.
-template <int TG, int kCS, int kS>
+template <int TG, int kCS, int kS, int kEB>
 constexpr int router_lds_body() {
-  constexpr int ring = kS * (kMaxExperts + 16 * TG) * kCS * 64;
-  constexpr int part = 4 * 16 * TG * (kMaxExperts + 1) * 4;
+  constexpr int ring = kS * (16 * kEB + 16 * TG) * kCS * 64;
+  constexpr int part = 4 * 16 * TG * (16 * kEB + 1) * 4;
   return ring > part ? ring : part;
 }
 
-template <int TG, int kCS, int kS>
+template <int TG, int kCS, int kS, int kEB>
 __global__ __launch_bounds__(256) void router_lds_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int E, int k, float scale,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ chunk_counts) {
   static_assert(kCS == 4 || kCS == 8, "row segments of 16 or 32 pieces");
+  static_assert(kEB == 4 || kEB == 8, "64 or 128 expert rows");
   constexpr int TM = 16 * TG;
-  constexpr int kRows = kMaxExperts + TM;        // the router weight's rows, then the tokens'
+  constexpr int kER = 16 * kEB;                  // expert rows (one or two per lane)
+  constexpr int kRows = kER + TM;                // the router weight's rows, then the tokens'
   constexpr int kSeg = kCS * 64;                 // bytes of a row per chunk
   constexpr int kLanesRow = kSeg / 16;           // lanes (16-byte pieces) per row segment
   constexpr int kRowsLoad = 64 / kLanesRow;      // row segments per 1 KB load
@@ -142,12 +205,13 @@ __global__ __launch_bounds__(256) void router_lds_kernel(
   constexpr int kLoads = kRows / kRowsLoad / 4;  // direct loads per wave per chunk
   static_assert(kRows % (4 * kRowsLoad) == 0, "loads split evenly over the waves");
   static_assert((kS - 2) * kLoads < 64, "vmcnt range");
-  constexpr int kPad = kMaxExperts + 1;
-  // Dynamic LDS (router_lds_smem bytes): the stages (later the class
-  // partials), then the histogram.  (With a static array, the compiler makes
-  // every fragment read wait for all of the ring's outstanding direct loads.)
+  constexpr int kPad = kER + 1;
+  // Dynamic LDS (router_lds_body bytes, then kER ints): the stages (later the
+  // class partials), then the histogram.  (With a static array, the compiler
+  // makes every fragment read wait for all of the ring's outstanding direct
+  // loads.)
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  int* hist = reinterpret_cast<int*>(smem + router_lds_body<TG, kCS, kS>());
+  int* hist = reinterpret_cast<int*>(smem + router_lds_body<TG, kCS, kS, kEB>());
 
   const int lane = threadIdx.x & 63;
   const int rc = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -156,9 +220,11 @@ __global__ __launch_bounds__(256) void router_lds_kernel(
   const int steps = d / 32;
   const int nch = ceil_div(steps, kCS);
 
-  if (threadIdx.x < kMaxExperts) hist[threadIdx.x] = 0;
-  // The selection bias, requested now so that its latency hides behind the loop.
+  if (threadIdx.x < kER) hist[threadIdx.x] = 0;
+  // The selection biases, requested now so that their latency hides behind
+  // the loop.
   const float b_lane = (bias != nullptr && lane < E) ? bias[lane] : 0.f;
+  const float b_lane1 = (kEB == 8 && bias != nullptr && lane + 64 < E) ? bias[lane + 64] : 0.f;
 
   // This lane's part of its direct loads: load i fills row segments
   // (rc * kLoads + i) * kRowsLoad ..; the lane's 16 B land at physical piece
@@ -171,8 +237,8 @@ __global__ __launch_bounds__(256) void router_lds_kernel(
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int row = (rc * kLoads + i) * kRowsLoad + lane / kLanesRow;
-    src[i] = row < kMaxExperts ? wr + (size_t)min(row, E - 1) * d
-                               : x + (size_t)min(t0 + row - kMaxExperts, T - 1) * d;
+    src[i] = row < kER ? wr + (size_t)min(row, E - 1) * d
+                       : x + (size_t)min(t0 + row - kER, T - 1) * d;
     off[i] = (((lane % kLanesRow) ^ (row & 15))) * 8;
   }
   auto issue = [&](int j) {
@@ -184,11 +250,11 @@ __global__ __launch_bounds__(256) void router_lds_kernel(
                                        (lds_void*)(stage + (rc * kLoads + i) * 1024), 16, 0, 0);
   };
 
-  f32x4 acc[TG][4];
+  f32x4 acc[TG][kEB];
 #pragma unroll
   for (int g = 0; g < TG; ++g)
 #pragma unroll
-    for (int eb = 0; eb < 4; ++eb) acc[g][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int eb = 0; eb < kEB; ++eb) acc[g][eb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Chunk j: wait for this wave's loads of it (those of the next kS - 2
   // chunks may stay in flight) and its LDS reads, barrier (every wave's loads
@@ -207,16 +273,16 @@ __global__ __launch_bounds__(256) void router_lds_kernel(
       const int sl = 4 * u + rc;  // the wave's step within the chunk
       if (j * kCS + sl < steps) {
         const int pc = (((sl * 4 + q) ^ r16)) << 4;
-        Frag16 b[4];
+        Frag16 b[kEB];
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb)
+        for (int eb = 0; eb < kEB; ++eb)
           b[eb].u = *reinterpret_cast<const u32x4*>(stage + (eb * 16 + r16) * kSeg + pc);
 #pragma unroll
         for (int g = 0; g < TG; ++g) {
           Frag16 a;
-          a.u = *reinterpret_cast<const u32x4*>(stage + (kMaxExperts + g * 16 + r16) * kSeg + pc);
+          a.u = *reinterpret_cast<const u32x4*>(stage + (kER + g * 16 + r16) * kSeg + pc);
 #pragma unroll
-          for (int eb = 0; eb < 4; ++eb) acc[g][eb] = mfma16x16x32(a.h, b[eb].h, acc[g][eb]);
+          for (int eb = 0; eb < kEB; ++eb) acc[g][eb] = mfma16x16x32(a.h, b[eb].h, acc[g][eb]);
         }
       }
     }
@@ -228,22 +294,30 @@ __global__ __launch_bounds__(256) void router_lds_kernel(
 #pragma unroll
   for (int g = 0; g < TG; ++g)
 #pragma unroll
-    for (int eb = 0; eb < 4; ++eb)
+    for (int eb = 0; eb < kEB; ++eb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) part[rc][g * 16 + q * 4 + i][eb * 16 + r16] = acc[g][eb][i];
   __syncthreads();
 
   // Wave rc selects for tokens rc, rc + 4, rc + 8, ... of the tile.
   constexpr int NT = TM / 4;
-  float logit[NT];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const int r = rc + 4 * i;
-    logit[i] = ((part[0][r][lane] + part[1][r][lane]) + part[2][r][lane]) + part[3][r][lane];
-  }
   int my_idx[NT];
   float my_w[NT];
-  topk_tokens<NT>(logit, b_lane, lane, E, k, scale, my_idx, my_w);
+  {
+    float logit[NT], logit1[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int r = rc + 4 * i;
+      logit[i] = ((part[0][r][lane] + part[1][r][lane]) + part[2][r][lane]) + part[3][r][lane];
+      if constexpr (kEB == 8)
+        logit1[i] = ((part[0][r][lane + 64] + part[1][r][lane + 64]) + part[2][r][lane + 64]) +
+                    part[3][r][lane + 64];
+    }
+    if constexpr (kEB == 8)
+      topk_tokens2<NT>(logit, logit1, b_lane, b_lane1, lane, E, k, scale, my_idx, my_w);
+    else
+      topk_tokens<NT>(logit, b_lane, lane, E, k, scale, my_idx, my_w);
+  }
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int t = t0 + rc + 4 * i;
@@ -294,11 +368,11 @@ static RouterChoice router_choice(int T) {
 
 int router_chunk_tokens(int T) { return router_choice(T).tokens; }  // >= 16 for every choice
 
-template <int TG, int kS>
+template <int TG, int kS, int kEB = 4>
 static hipError_t launch_lds_config(const RouterArgs& a, hipStream_t stream) {
   constexpr int kCS = 4;
-  auto kern = router_lds_kernel<TG, kCS, kS>;
-  constexpr int smem = router_lds_body<TG, kCS, kS>() + kMaxExperts * 4;
+  auto kern = router_lds_kernel<TG, kCS, kS, kEB>;
+  constexpr int smem = router_lds_body<TG, kCS, kS, kEB>() + 16 * kEB * 4;
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t err = once_per_device(attr_done, [&]() {
     return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
@@ -317,6 +391,13 @@ hipError_t launch_router_lds(const RouterArgs& a, hipStream_t stream) {
     return launch_lds_config<2, 3>(a, stream);
   }
   return launch_lds_config<4, 2>(a, stream);
+}
+
+// The FFN router's configuration (up to 128 experts, two per selecting lane):
+// 16 tokens per workgroup, the FFN's dispatch chunk.
+hipError_t launch_router_lds_wide(const RouterArgs& a, hipStream_t stream) {
+  if (a.E > 128) return hipErrorInvalidValue;
+  return launch_lds_config<1, 3, 8>(a, stream);
 }
 
 // ---- small T: the same chains spread over many single-wave workgroups ------

@@ -129,6 +129,37 @@ def test_ffn_rows_do_not_depend_on_other_tokens():
     assert torch.equal(full, again)
 
 
+@pytest.mark.parametrize("E,k,ties", [(100, 8, None), (128, 8, "planes"), (100, 8, "pairs"),
+                                      (12, 3, None), (64, 4, None), (65, 5, "planes")])
+def test_ffn_router_kernels_bitwise(E, k, ties):
+    """From 1024 tokens on, the FFN routes with the LDS-staged router (two
+    experts per selecting lane); below, with its two-kernel router.  Both give
+    the same routing bits: a call of 1536 tokens against calls on slices of
+    it, also with experts j and j + 64 tied (the two lanes' planes) or
+    experts 2j and 2j + 1 tied (lower index first)."""
+    sh = inputs.FfnShape(T=1536, d=512, E=E, k=k, inter=64, inter_shared=0)
+    L, g = gpu_layer(sh, seed=E + k)
+    if ties == "planes" and E > 64:
+        g["router_w"][64:E] = g["router_w"][0:E - 64]
+        g["router_b"].zero_()
+    elif ties == "pairs":
+        g["router_w"][1::2] = g["router_w"][0::2][: E // 2]
+        g["router_b"].zero_()
+    say(f"ffn router E={E} k={k} ties={ties}")
+    _, idx, w = run_ffn(g, sh)
+    for a, b in ((0, 700), (700, 1400), (1400, 1536)):
+        _, i2, w2 = run_ffn(g, sh, g["x"][a:b].contiguous())
+        assert torch.equal(idx[a:b], i2) and torch.equal(w[a:b], w2), (a, b)
+    rows = idx.cpu().tolist()
+    for row in rows:
+        assert len(set(row)) == k
+        for pos, e in enumerate(row):
+            if ties == "planes" and e >= 64:
+                assert e - 64 in row[:pos], f"plane tie order broken in {row}"
+            if ties == "pairs" and e % 2 == 1:
+                assert e - 1 in row[:pos], f"pair tie order broken in {row}"
+
+
 @pytest.mark.parametrize("T,d,E,k,inter,inter_s", [
     (64, 2560, 100, 8, 768, 768),
     (1, 256, 12, 3, 64, 64),
