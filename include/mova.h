@@ -375,7 +375,9 @@ enum mova_override {
                                       stages, 5: with 4 stages, 6: 128x128 on 4 waves,
                                       7: 352x256 (routed GEMMs only) */
   MOVA_OVERRIDE_DENSE_PATH = 3,    /* 1: split-k kernel (T <= 256), 2: tiled GEMM */
-  MOVA_OVERRIDE_DECODE_CHAIN = 4,  /* 1: chain kernel wherever it fits, 2: never */
+  MOVA_OVERRIDE_DECODE_CHAIN = 4,  /* small-T expert kernel: 1: the chain kernel wherever it
+                                      fits, 2: neither it nor the token-major kernel, 3: the
+                                      token-major kernel (combine fused) wherever it fits */
   MOVA_OVERRIDE_DECODE_GROUPS = 5, /* 1 or 2: 16-column groups per wave in the decode kernel */
   MOVA_OVERRIDE_SERIAL = 6,        /* 1: the FFN's shared expert on the caller's stream */
   MOVA_OVERRIDE_COUNT = 7

@@ -503,7 +503,7 @@ OVERRIDES = {
     "gemm_tile": (2, {"256x256": 1, "128x256": 2, "128x128": 3, "128x128s3": 4,
                       "128x128s4": 5, "128x128w4": 6, "352x256": 7}),
     "dense_path": (3, {"skinny": 1, "tiled": 2}),
-    "decode_chain": (4, {"on": 1, "off": 2}),
+    "decode_chain": (4, {"on": 1, "off": 2, "token": 3}),
     "decode_groups": (5, {"1": 1, "2": 2}),
     "serial": (6, {"on": 1}),
 }

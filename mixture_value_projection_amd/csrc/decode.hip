@@ -351,6 +351,211 @@ __global__ __launch_bounds__(64 * kWaves) void decode_chain_kernel(
   }
 }
 
+// ---- few tokens, many experts each: token-major, the combine fused ---------
+//
+// With a handful of tokens the per-expert kernels above spread each token's k
+// weight reads over k workgroups, and a separate combine then sums the k
+// partial rows.  Here a workgroup owns one (token, 16-column group) and runs
+// all of that token's k chains, one slot per wave (two for k > 4), so the
+// k-way combine happens in the workgroup: fp16(w * SiLU(z)) of each slot,
+// widened and summed in slot order, rounded once to bf16 -- the combine
+// kernel's arithmetic.  Each chain is the one of the other kernels (token in
+// the MFMA's rows, here all 16 rows, the same steps in the same order), so
+// the bits are the same.
+//
+// A slot's 16 weight rows stream through a ring of kS LDS stages private to
+// its wave: chunk j holds k steps 4j .. 4j + 3 (256 B of each row), copied
+// by 1 KB direct loads of whole row segments (16 lanes per row), the piece p
+// of row r at p ^ (r & 15) so that the 16 rows a fragment read touches fall
+// in distinct bank groups.  Each wave also keeps its own copy of the token's
+// row in LDS (the A fragment is one 64-byte piece read by all 16 rows).  No
+// wave reads another's stages, so the loop has no barrier, only the wave's
+// own counter waits.  Slots whose expert id is outside [0, E) (caller's
+// routing) load expert 0's rows and add nothing.
+constexpr int kTokSeg = 4 * 64;          // bytes of a row per chunk (4 k steps)
+constexpr int kTokSlot = 16 * kTokSeg;   // one slot's 16 rows per chunk
+constexpr int kTokHeader = 512;          // ids, weights, the slots' fp16 rows
+
+__host__ __device__ inline int tok_x_bytes(int d) { return ceil_div(d * 2, 1024) * 1024; }
+template <int kSW, int kS>
+static int tok_smem(int d) { return kTokHeader + 4 * (tok_x_bytes(d) + kS * kSW * kTokSlot); }
+
+template <int kSW, int kS>  // kSW: slots per wave (k <= 4 * kSW); kS: ring stages
+__global__ __launch_bounds__(256) void decode_token_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const int32_t* __restrict__ idx,
+    const float* __restrict__ topk_w, bf16_t* __restrict__ out, const int64_t* __restrict__ slot,
+    long long num_slots, bf16_t* __restrict__ cache, int T, int d, int N, int E, int k) {
+  constexpr int kLoads = 4 * kSW;  // direct loads per wave per chunk
+  static_assert((kS - 2) * kLoads < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  int* sh_e = reinterpret_cast<int*>(smem);                 // [8]
+  float* sh_w = reinterpret_cast<float*>(smem + 32);        // [8]
+  f16_t* sh_p = reinterpret_cast<f16_t*>(smem + 64);        // [8][16]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, r16 = lane & 15;
+  const int groups = N / 16;
+  const int t = blockIdx.x / groups;
+  const int n0 = (blockIdx.x % groups) * 16;
+  const int xb = tok_x_bytes(d);
+  char* region = smem + kTokHeader + wave * (xb + kS * kSW * kTokSlot);
+  char* ring = region + xb;
+  const int steps = d / 32;
+  const int nch = ceil_div(steps, 4);
+
+  if (tid < k) {
+    sh_e[tid] = idx[(size_t)t * k + tid];
+    sh_w[tid] = topk_w[(size_t)t * k + tid];
+  }
+  __syncthreads();
+
+  // The token's row into this wave's copy (element order kept; the last
+  // load's lanes past d repeat the row's last piece, never read).
+  const bf16_t* xrow = x + (size_t)t * d;
+  for (int i = 0; i < xb / 1024; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(xrow + min(i * 512 + lane * 8, d - 8)),
+                                     (lds_void*)(region + i * 1024), 16, 0, 0);
+
+  // This wave's slots and the source of its lane in each direct load: load
+  // i of slot s covers rows 4i .. 4i + 3, the lane's row 4i + lane / 16 and
+  // logical piece (lane % 16) ^ (row & 15).
+  int sj[kSW];
+  bool valid[kSW];
+  const bf16_t* src[kSW][4];
+  int off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + lane / 16;
+    off[i] = ((lane % 16) ^ row) * 8;
+  }
+#pragma unroll
+  for (int s = 0; s < kSW; ++s) {
+    sj[s] = wave + 4 * s;
+    const int e = sj[s] < k ? sh_e[sj[s]] : -1;
+    valid[s] = e >= 0 && e < E;
+    const int ee = valid[s] ? e : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      src[s][i] = W + ((size_t)ee * N + n0 + 4 * i + lane / 16) * d;
+  }
+  auto issue = [&](int j) {
+    char* stage = ring + (j % kS) * (kSW * kTokSlot);
+#pragma unroll
+    for (int s = 0; s < kSW; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(src[s][i] + min(j * 128 + off[i], d - 8)),
+                                         (lds_void*)(stage + s * kTokSlot + i * 1024), 16, 0, 0);
+  };
+
+  f32x4 acc[kSW];
+#pragma unroll
+  for (int s = 0; s < kSW; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kS - 1 && j < nch; ++j) issue(j);
+  for (int j = 0; j < nch; ++j) {
+    if (j + kS - 2 < nch) __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm((kS - 2) * kLoads));
+    else __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("" ::: "memory");
+    const char* stage = ring + (j % kS) * (kSW * kTokSlot);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int st = 4 * j + u;
+      if (st < steps) {
+        Frag16 a;
+        a.u = *reinterpret_cast<const u32x4*>(region + (st * 32 + 8 * q) * 2);
+#pragma unroll
+        for (int s = 0; s < kSW; ++s) {
+          if (valid[s]) {
+            Frag16 b;
+            b.u = *reinterpret_cast<const u32x4*>(stage + s * kTokSlot + r16 * kTokSeg +
+                                                  (((u * 4 + q) ^ r16) << 4));
+            acc[s] = mfma16x16x32(a.h, b.h, acc[s]);
+          }
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+    if (j + kS - 1 < nch) issue(j + kS - 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  // Row 0 of each chain (lanes 0 .. 15, element 0) is the token's z.
+  if (lane < 16) {
+#pragma unroll
+    for (int s = 0; s < kSW; ++s)
+      if (valid[s]) sh_p[sj[s] * 16 + lane] = (f16_t)(sh_w[sj[s]] * siluf(acc[s][0]));
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float sum = 0.f;
+    bool first = true;
+    for (int j = 0; j < k; ++j) {
+      const int e = sh_e[j];
+      if (e < 0 || e >= E) continue;
+      const float v = (float)sh_p[j * 16 + tid];
+      sum = first ? v : sum + v;
+      first = false;
+    }
+    const bf16_t r = (bf16_t)sum;
+    if (out != nullptr) out[(size_t)t * N + n0 + tid] = r;
+    if (cache != nullptr) {
+      const long long sl = slot[t];
+      if (sl >= 0 && sl < num_slots) cache[(size_t)sl * N + n0 + tid] = r;
+    }
+  }
+}
+
+// Whether the token-major kernel takes a call (value experts): 0 = no, else
+// its ring stages.  Measured at d = 2560, N = 1024, k = 4 (graph replay, 4
+// weight copies; per-expert kernels and the combine, the best of them, vs
+// this kernel with 4 / 3 stages), call times in us:
+//   T          1     2     4     6     8     12    16    24    32
+//   others     16.5  20.3  29.6  37.2  43.7  58.9  62.1  64.6  66.0
+//   4 stages   14.9  16.1  21.0  31.1  36.2  49.5  60.0  81.9  104.0
+//   3 stages   16.2  -     21.5  -     34.3  49.0  54.7  -     -
+// so it takes T * k <= 64, with 4 stages (84 KB of LDS, one workgroup per
+// CU) while its workgroups fit in one per CU and 3 (68 KB, two per CU)
+// beyond.  kOvDecodeChain = 3 forces it wherever it fits, 1 and 2 keep it
+// off.
+int decode_token_stages(int T, int d, int N, int E, int k) {
+  (void)E;
+  const int ov = override_value(kOvDecodeChain);
+  if (ov == 1 || ov == 2) return 0;
+  if (k > 8 || N % 16 != 0 || d % 64 != 0) return 0;
+  if (ov != 3 && (long long)T * k > 64) return 0;
+  if (k > 4) return tok_smem<2, 3>(d) <= 160 * 1024 ? 3 : 0;
+  const int st = (long long)T * (N / 16) <= 256 ? 4 : 3;
+  if (st == 4 && tok_smem<1, 4>(d) <= 160 * 1024) return 4;
+  return tok_smem<1, 3>(d) <= 160 * 1024 ? 3 : 0;
+}
+
+template <int kSW, int kS>
+static hipError_t launch_token_cfg(const DecodeTokenArgs& a, hipStream_t stream) {
+  auto kern = decode_token_kernel<kSW, kS>;
+  const int smem = tok_smem<kSW, kS>(a.d);
+  static std::atomic<unsigned long long> attr_done{0};
+  hipError_t err = once_per_device(attr_done, [&]() {
+    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               160 * 1024);
+  });
+  if (err != hipSuccess) return err;
+  kern<<<dim3((unsigned)(a.T * (a.N / 16))), 256, smem, stream>>>(
+      a.x, a.W, a.idx, a.topk_w, a.out, a.slot, a.num_slots, a.cache, a.T, a.d, a.N, a.E, a.k);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_token(const DecodeTokenArgs& a, int stages, hipStream_t stream) {
+  if (a.k > 8 || a.N % 16 != 0 || a.d % 64 != 0 || a.T > kDecodeMaxT) return hipErrorInvalidValue;
+  if (a.k > 4) {
+    if (stages != 3 || tok_smem<2, 3>(a.d) > 160 * 1024) return hipErrorInvalidValue;
+    return launch_token_cfg<2, 3>(a, stream);
+  }
+  if (stages == 4 && tok_smem<1, 4>(a.d) <= 160 * 1024) return launch_token_cfg<1, 4>(a, stream);
+  if (stages == 3 && tok_smem<1, 3>(a.d) <= 160 * 1024) return launch_token_cfg<1, 3>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 // Whether the chain kernel takes a call: 0, or its k steps per wave.  The
 // SwiGLU epilogue holds two groups of weights, so it splits k over 8 waves.
 // T * k up to which it is the default, measured: the value experts (d =
@@ -361,8 +566,9 @@ __global__ __launch_bounds__(64 * kWaves) void decode_chain_kernel(
 static int chain_auto_pairs(int mode) { return mode == kGemmRoutedSilu ? 16 : 32; }
 static int chain_waves(int mode) { return mode == kGemmRoutedSwiGLU ? 8 : 4; }
 static int chain_steps_per_wave(const DecodeArgs& a) {
-  const int ov = override_value(kOvDecodeChain);  // 1 / 2 force it on / off (tests, measurement)
-  const bool force_on = ov == 1, force_off = ov == 2;
+  // 1 / 2 force it on / off (tests, measurement); 3 forces the token-major kernel.
+  const int ov = override_value(kOvDecodeChain);
+  const bool force_on = ov == 1, force_off = ov == 2 || ov == 3;
   const int per = ceil_div(a.d / 32, chain_waves(a.mode));
   const int max_per = a.mode == kGemmRoutedSwiGLU ? 16 : 24;  // registers (two groups)
   const bool fits = (long long)a.T * a.k <= kChainMaxPairs && a.E <= 128 &&

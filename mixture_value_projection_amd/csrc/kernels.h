@@ -166,6 +166,24 @@ struct DecodeArgs {
 constexpr int kDecodeMaxT = 256;
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Token-major small-T value experts with the k-way combine fused: writes the
+// bf16 rows to out (if not null) and to cache row slot[t] (if cache is set
+// and 0 <= slot[t] < num_slots).  decode_token_stages: 0 when the kernel does
+// not take the call (by shape, the automatic choice or kOvDecodeChain).
+struct DecodeTokenArgs {
+  const __bf16* x;       // [T, d]
+  const __bf16* W;       // [E, N, d]
+  const int32_t* idx;    // [T, k]; ids outside [0, E) add nothing
+  const float* topk_w;   // [T, k]
+  __bf16* out;           // [T, N] or null
+  const int64_t* slot = nullptr;
+  long long num_slots = 0;
+  __bf16* cache = nullptr;
+  int T, d, N, E, k;
+};
+int decode_token_stages(int T, int d, int N, int E, int k);
+hipError_t launch_decode_token(const DecodeTokenArgs& a, int stages, hipStream_t stream);
+
 struct CombineArgs {
   const f16_t* partial;  // [T * k, N]
   __bf16* out;           // [T, N]; may be null when cache is set

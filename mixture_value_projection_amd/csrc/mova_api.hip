@@ -45,7 +45,7 @@ enum class Path { Decode, Grouped };
 
 // Kernel-choice overrides (mova_debug_override); largest value per key.
 std::atomic<int> g_override[kOvCount];
-constexpr int kOverrideMax[kOvCount] = {2, 4, 7, 2, 2, 2, 1};
+constexpr int kOverrideMax[kOvCount] = {2, 4, 7, 2, 3, 2, 1};
 
 // Path forced by the kOvPath override: 1 the decode kernel (where T allows
 // it), 2 dispatch and the grouped GEMM; 0 when none applies.
@@ -458,6 +458,18 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
 
   if (path == Path::Decode) {
     StageScope sc(2, stream);
+    if (const int stages = decode_token_stages(T, d, N, E, k)) {
+      // Token-major kernel: the k-way combine is fused into it.
+      DecodeTokenArgs ta{xb, wb, idx, w, (__bf16*)out};
+      ta.T = T; ta.d = d; ta.N = N; ta.E = E; ta.k = k;
+      if (pg != nullptr) {
+        ta.slot = pg->slot;
+        ta.num_slots = (long long)pg->num_blocks * pg->block_size;
+        ta.cache = (__bf16*)pg->cache;
+      }
+      err = launch_decode_token(ta, stages, stream);
+      return err == hipSuccess ? MOVA_OK : MOVA_ERR_HIP;
+    }
     DecodeArgs da{xb, wb, idx, w, partial, T, d, N, E, k};
     err = launch_decode(da, stream);
   } else {

@@ -206,8 +206,9 @@ def test_decode_column_groups_bitwise(groups, T, d, E, k, heads, hd):
                                               (5, 64, 7, 3, 1, 64), (2, 256, 64, 1, 1, 128),
                                               (16, 512, 40, 4, 4, 64)])
 def test_decode_chain_kernel_bitwise(T, d, E, k, heads, hd):
-    """The small-T kernel (a chain's k steps split over four waves, the
-    accumulator handed on) gives the grouped path's bits."""
+    """The small-T kernels (a chain's k steps split over four waves, the
+    accumulator handed on; and token-major with the combine fused) give the
+    grouped path's bits."""
     shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=heads, head_dim=hd)
     g = {n: v.to(DEV) for n, v in inputs.make_layer(shape, 7 * T + d, torch.bfloat16, "uniform").items()}
     print(f"decode chain T={T} d={d} E={E} k={k} N={heads * hd}", flush=True)
@@ -215,8 +216,11 @@ def test_decode_chain_kernel_bitwise(T, d, E, k, heads, hd):
     dec = _run(g, k, heads, hd, {"path": "decode"})
     binding.set_override("decode_chain", "off")
     reg = _run(g, k, heads, hd, {"path": "decode"})
+    binding.set_override("decode_chain", "token")
+    tok = _run(g, k, heads, hd, {"path": "decode"})
     binding.set_override("decode_chain", None)
     grp = _run(g, k, heads, hd, {"path": "grouped"})
-    for name, a, b, c in zip(("out", "idx", "w"), dec, reg, grp):
+    for name, a, b, c, e in zip(("out", "idx", "w"), dec, reg, grp, tok):
         assert torch.equal(a, c), f"{name}: chain kernel differs from the grouped path"
         assert torch.equal(b, c), f"{name}: decode kernel differs from the grouped path"
+        assert torch.equal(e, c), f"{name}: token-major kernel differs from the grouped path"

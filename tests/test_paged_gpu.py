@@ -77,6 +77,8 @@ CASES = [
     (64, 2560, 64, 4, 8, 128, 12, 16, "decode"),
     (64, 2560, 64, 4, 8, 128, 12, 16, "grouped"),
     (37, 256, 16, 4, 2, 64, 5, 8, "decode"),
+    (8, 2560, 64, 4, 8, 128, 12, 16, "decode"),   # token-major decode kernel (T * k <= 64)
+    (3, 256, 16, 4, 2, 64, 5, 8, "decode"),
     (300, 512, 32, 4, 4, 64, 40, 16, "grouped"),
     (1000, 256, 8, 2, 1, 64, 1100, 1, "grouped"),
     (4096, 2560, 64, 4, 8, 128, 160, 32, "grouped"),
@@ -113,9 +115,9 @@ def test_paged_store_matches_oracle(T, d, E, k, H, D, nb, bs, path):
     say(f"  pool: {len(valid)} rows stored, {len(untouched)} untouched")
 
 
-@pytest.mark.parametrize("path", ["decode", "grouped"])
-def test_paged_without_out_equals_plain_forward(path):
-    T, d, E, k, H, D, nb, bs = 200, 2560, 64, 4, 8, 128, 16, 16
+@pytest.mark.parametrize("path,T", [("decode", 200), ("grouped", 200), ("decode", 12)])
+def test_paged_without_out_equals_plain_forward(path, T):
+    d, E, k, H, D, nb, bs = 2560, 64, 4, 8, 128, 16, 16
     shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=H, head_dim=D)
     g = P.to_gpu_inputs(inputs.make_layer(shape, 21, torch.bfloat16, "uniform"))
     slots = make_slots(T, nb * bs, seed=4, pad_every=5)

@@ -46,6 +46,8 @@ def with_path(path, fn):
 
 SHAPES = [
     # T, d, E, k, H, D
+    (8, 2560, 64, 4, 8, 128),      # token-major decode kernel (T * k <= 64)
+    (5, 256, 8, 3, 2, 32),
     (37, 256, 8, 2, 2, 32),
     (64, 2560, 64, 4, 8, 128),
     (300, 512, 16, 4, 2, 64),
@@ -106,8 +108,9 @@ def test_rebuild_stored_routing_matches_oracle(T, d, E, k, H, D):
         assert torch.equal(outs["grouped"], outs["decode"])
 
 
-def test_rebuild_all_slots_unused_is_zero():
-    T, d, E, k, H, D = 90, 256, 8, 3, 2, 64
+@pytest.mark.parametrize("T", [90, 10])
+def test_rebuild_all_slots_unused_is_zero(T):
+    d, E, k, H, D = 256, 8, 3, 2, 64
     shape = inputs.LayerShape(T=T, d=d, E=E, k=k, n_kv_heads=H, head_dim=D)
     g = P.to_gpu_inputs(inputs.make_layer(shape, 3, torch.bfloat16, "uniform"))
     gi = torch.full((T, k), -1, dtype=torch.int32, device=DEV)
