@@ -96,27 +96,42 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
       }
     }
   }
-  __syncthreads();
+  // The totals are in LDS; the offset stores above may still be in flight
+  // (nothing below reads them), so the barrier waits for LDS work only.
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(63));
+  raw_barrier();
   if (w == 0) {
-    // Expert offsets and first M-tiles: thread e sums the experts before it
-    // (entries past E are zero).
-    int off = 0, tiles = 0, all = 0, all_tiles = 0;
-#pragma unroll 16
-    for (int i = 0; i < cols; ++i) {
-      const int t = total[i];
-      const int mt = mtiles[i];
-      off += i < e ? t : 0;
-      tiles += i < e ? mt : 0;
-      all += t;
-      all_tiles += mt;
+    // Expert offsets and first M-tiles: exclusive prefix sums over the
+    // experts (entries past E are zero), by an inclusive scan across each
+    // wave's lanes; with 128 columns the second wave adds the first wave's
+    // sum, which it reduces itself from the same table.
+    const int lane = threadIdx.x & 63;
+    int it = total[e], imt = mtiles[e];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int a = __shfl_up(it, o, 64), b = __shfl_up(imt, o, 64);
+      if (lane >= o) {
+        it += a;
+        imt += b;
+      }
+    }
+    if (e >= 64) {
+      int st = total[lane], smt = mtiles[lane];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        st += __shfl_xor(st, o, 64);
+        smt += __shfl_xor(smt, o, 64);
+      }
+      it += st;
+      imt += smt;
     }
     if (e < E) {
-      expert_off[e] = off;
-      tile_base[e] = tiles;
+      expert_off[e] = it - total[e];
+      tile_base[e] = imt - mtiles[e];
     }
-    if (e == 0) {
-      expert_off[E] = all;
-      tile_base[E] = all_tiles;
+    if (e == cols - 1) {
+      expert_off[E] = it;
+      tile_base[E] = imt;
     }
   }
 }
