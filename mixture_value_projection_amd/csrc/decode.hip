@@ -16,7 +16,10 @@
 // share one token fragment; per 32-wide k step its 64 lanes read 2 x 16 rows x
 // 64 B of weights and one 16-byte token fragment (token row = lane % 16, read
 // straight from cache: the rows are a few hundred KB shared by the whole
-// grid).  The k loop runs in batches of kUnroll steps over a ring of three
+// grid).  With 4-step batches and one row group, the weights are loaded as
+// whole 256-byte row segments (16 lanes per row, which the vector cache
+// serves with far fewer requests than 16 rows per 16 lanes) and turned into
+// fragments through a small LDS scratch of the wave's own.  The k loop runs in batches of kUnroll steps over a ring of three
 // register buffers, so three batches of loads are in flight while a batch's
 // MFMAs run; the waves never wait for each other inside the loop.  The first
 // two weight batches are issued before the routing scan, which they do not
@@ -70,6 +73,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ int plist[kDecodeMaxT * kMaxTopK];
   __shared__ float wlist[kDecodeMaxT * kMaxTopK];
   __shared__ int wave_hits[4];
+  // Weight loads as whole row segments, turned into MFMA fragments through a
+  // wave-private LDS scratch (4-step batches with one row group; measured:
+  // 62.1 -> 60.4 us at T = 64, but 71 -> 75 us with the two-deep ring of
+  // 32-pair passes, where the extra LDS round trip is not hidden).
+  constexpr bool kRowLoads = kUnroll == 4 && !kPair32;
+  __shared__ __attribute__((aligned(16))) char wscr[kRowLoads ? 4 : 1][kRowLoads ? kGroups * 16 * 256 : 16];
 
   static_assert(kGroups == 2 || (kGroups == 1 && kMode != kGemmRoutedSwiGLU),
                 "SwiGLU pairs a gate group with its up group in one wave");
@@ -87,18 +96,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // load a clamped row and are never stored.
   int ncol[kGroups];
   const bf16_t* wrow[kGroups];
+  const bf16_t* wseg[kGroups][4];
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
     ncol[g] = n0 + wave * 16 * kGroups + g * 16 + r16;
     wrow[g] = W + ((size_t)e * N + min(ncol[g], N - 1)) * d + q * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wseg[g][i] = W +
+                   ((size_t)e * N + min(n0 + wave * 16 * kGroups + g * 16 + 4 * i + (lane >> 4), N - 1)) * d +
+                   (lane & 15) * 8;
   }
   const int nb = d / 32 / kUnroll;  // exact by the choice of kUnroll
   auto load_w = [&](Frag16 (&b)[kGroups][kUnroll], int bt) {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-      const bf16_t* p = wrow[g] + (size_t)bt * kUnroll * 32;
+      if constexpr (kRowLoads) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) b[g][u].u = load16(p + u * 32);
+        for (int i = 0; i < 4; ++i) b[g][i].u = load16(wseg[g][i] + (size_t)bt * 128);
+      } else {
+        const bf16_t* p = wrow[g] + (size_t)bt * kUnroll * 32;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) b[g][u].u = load16(p + u * 32);
+      }
     }
   };
   Frag16 b0[kGroups][kUnroll], b1[kGroups][kUnroll], b2[kGroups][kUnroll];
@@ -168,13 +188,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int g = 0; g < kGroups; ++g) acc[rg][g] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Batch bt's MFMAs from (bc, xc), then refill them with batch bt + kRing.
     auto batch = [&](int bt, Frag16 (&bc)[kGroups][kUnroll], Frag16 (&xc)[RG][kUnroll]) {
+      Frag16 bf[kGroups][kUnroll];
+      if constexpr (kRowLoads) {
+        char* scr = wscr[wave];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * g + 4 * i + (lane >> 4);
+            *reinterpret_cast<u32x4*>(scr + row * 256 + ((((lane & 15) ^ (row & 15))) << 4)) = bc[g][i].u;
+          }
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(63));
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u)
+            bf[g][u].u = *reinterpret_cast<const u32x4*>(scr + (16 * g + r16) * 256 + ((((4 * u + q) ^ r16)) << 4));
+      } else {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) bf[g][u] = bc[g][u];
+      }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
           for (int g = 0; g < kGroups; ++g)
-            acc[rg][g] = mfma16x16x32(xc[rg][u].h, bc[g][u].h, acc[rg][g]);
+            acc[rg][g] = mfma16x16x32(xc[rg][u].h, bf[g][u].h, acc[rg][g]);
       if (bt + kRing < nb) {
         load_w(bc, bt + kRing);
         load_x(xc, bt + kRing);
