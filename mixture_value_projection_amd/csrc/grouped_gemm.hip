@@ -113,11 +113,17 @@ GemmTile gemm_tile_grouped(int T, int k, int E, int N) {
   //   128x128  100  115  150  154  -    188  196  208  207  235  247  281  300  -    -
   //   256x256  114  119  124  137  202  201  197  -    209  212  218  285  289  299  350
   //   352x256  -    -    -    152  172  150  159  172  239  243  251  256  262  355  358
-  // 352 x 256 for R in (200, 272] and (408, 560] when E * N / 256 >= 256;
-  // otherwise 128 x 128 up to R = 112 and from 209 to 304, 256 x 256 elsewhere.
+  // and for larger R (one session, uniform routing, then the Zipf-skewed
+  // T = 32768 workload):
+  //   R        768  1024  1536  2048  skewed
+  //   256x256  375  455   642   848   831
+  //   352x256  366  460   605   814   819
+  // 352 x 256 for R in (200, 272], (408, 560] and above 704 when
+  // E * N / 256 >= 256; otherwise 128 x 128 up to R = 112 and from 209 to
+  // 304, 256 x 256 elsewhere.
   const long long R = ((long long)T * k + E / 2) / E;
   const bool fills = (long long)E * ceil_div(N, 256) >= 256;
-  if (fills && ((R > 200 && R <= 272) || (R > 408 && R <= 560))) return {352, 256, 8, 2};
+  if (fills && ((R > 200 && R <= 272) || (R > 408 && R <= 560) || R > 704)) return {352, 256, 8, 2};
   if (R <= 112 || (R > 208 && R <= 304)) return {128, 128, 8, 2};
   return {256, 256, 8, 2};
 }
