@@ -44,6 +44,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace mova {
 
@@ -422,11 +423,17 @@ __host__ __device__ inline int tok_x_bytes(int d) { return ceil_div(d * 2, 1024)
 template <int kSW, int kS>
 static int tok_smem(int d) { return kTokHeader + 4 * (tok_x_bytes(d) + kS * kSW * kTokSlot); }
 
-template <int kSW, int kS>  // kSW: slots per wave (k <= 4 * kSW); kS: ring stages
+// kRoute: the routing comes as the small-T router's class partials (plog, Tp
+// rows per class plane); wave 0 of each workgroup adds them in class order and
+// selects its token's top k with topk_tokens, the router's own selection, and
+// the workgroups of column group 0 also write the routing to idx / topk_w.
+template <int kSW, int kS, bool kRoute>  // kSW: slots per wave (k <= 4 * kSW); kS: ring stages
 __global__ __launch_bounds__(256) void decode_token_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, const int32_t* __restrict__ idx,
-    const float* __restrict__ topk_w, bf16_t* __restrict__ out, const int64_t* __restrict__ slot,
-    long long num_slots, bf16_t* __restrict__ cache, int T, int d, int N, int E, int k) {
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int32_t* __restrict__ idx,
+    float* __restrict__ topk_w, const float* __restrict__ plog, int Tp,
+    const float* __restrict__ bias, float scale, bf16_t* __restrict__ out,
+    const int64_t* __restrict__ slot, long long num_slots, bf16_t* __restrict__ cache, int T, int d,
+    int N, int E, int k) {
   constexpr int kLoads = 4 * kSW;  // direct loads per wave per chunk
   static_assert((kS - 2) * kLoads < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -447,18 +454,37 @@ __global__ __launch_bounds__(256) void decode_token_kernel(
   const int steps = d / 32;
   const int nch = ceil_div(steps, 4);
 
-  if (tid < k) {
-    sh_e[tid] = idx[(size_t)t * k + tid];
-    sh_w[tid] = topk_w[(size_t)t * k + tid];
-  }
-  __syncthreads();
-
   // The token's row into this wave's copy (element order kept; the last
-  // load's lanes past d repeat the row's last piece, never read).
+  // load's lanes past d repeat the row's last piece, never read).  It does
+  // not depend on the routing, so it is requested first.
   const bf16_t* xrow = x + (size_t)t * d;
   for (int i = 0; i < xb / 1024; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(xrow + min(i * 512 + lane * 8, d - 8)),
                                      (lds_void*)(region + i * 1024), 16, 0, 0);
+
+  if constexpr (kRoute) {
+    if (wave == 0) {
+      const size_t cls = (size_t)Tp * kMaxExperts;
+      const float* src = plog + (size_t)t * kMaxExperts + lane;
+      const float lg[1] = {((src[0] + src[cls]) + src[2 * cls]) + src[3 * cls]};
+      const float b_lane = (bias != nullptr && lane < E) ? bias[lane] : 0.f;
+      int my_idx[1];
+      float my_w[1];
+      topk_tokens<1>(lg, b_lane, lane, E, k, scale, my_idx, my_w);
+      if (lane < k) {
+        sh_e[lane] = my_idx[0];
+        sh_w[lane] = my_w[0];
+        if (n0 == 0) {
+          idx[(size_t)t * k + lane] = my_idx[0];
+          topk_w[(size_t)t * k + lane] = my_w[0];
+        }
+      }
+    }
+  } else if (tid < k) {
+    sh_e[tid] = idx[(size_t)t * k + tid];
+    sh_w[tid] = topk_w[(size_t)t * k + tid];
+  }
+  __syncthreads();
 
   // This wave's slots and the source of its lane in each direct load: load
   // i of slot s covers rows 4i .. 4i + 3, the lane's row 4i + lane / 16 and
@@ -574,16 +600,20 @@ int decode_token_stages(int T, int d, int N, int E, int k) {
 
 template <int kSW, int kS>
 static hipError_t launch_token_cfg(const DecodeTokenArgs& a, hipStream_t stream) {
-  auto kern = decode_token_kernel<kSW, kS>;
+  auto kern = a.plog != nullptr ? decode_token_kernel<kSW, kS, true> : decode_token_kernel<kSW, kS, false>;
   const int smem = tok_smem<kSW, kS>(a.d);
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t err = once_per_device(attr_done, [&]() {
-    return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               160 * 1024);
+    hipError_t e1 = hipFuncSetAttribute((const void*)decode_token_kernel<kSW, kS, true>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipError_t e2 = hipFuncSetAttribute((const void*)decode_token_kernel<kSW, kS, false>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    return e1 != hipSuccess ? e1 : e2;
   });
   if (err != hipSuccess) return err;
   kern<<<dim3((unsigned)(a.T * (a.N / 16))), 256, smem, stream>>>(
-      a.x, a.W, a.idx, a.topk_w, a.out, a.slot, a.num_slots, a.cache, a.T, a.d, a.N, a.E, a.k);
+      a.x, a.W, a.idx, a.topk_w, a.plog, a.Tp, a.bias, a.scale, a.out, a.slot, a.num_slots,
+      a.cache, a.T, a.d, a.N, a.E, a.k);
   return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@ hipError_t launch_router_lds_wide(const RouterArgs& a, hipStream_t stream);
 // Same bits as launch_router_lds.  plog: router_small_plog_floats(T) floats.
 int router_small_plog_floats(int T);
 hipError_t launch_router_small(const RouterArgs& a, float* plog, hipStream_t stream);
+// Its first kernel alone (the class partials, for a consumer that selects).
+hipError_t launch_router_partial(const RouterArgs& a, float* plog, hipStream_t stream);
 
 // Experts the dispatch kernels handle (the value router itself takes at most
 // kMaxExperts; routing of wider layers comes from their own router).
@@ -173,13 +175,20 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 struct DecodeTokenArgs {
   const __bf16* x;       // [T, d]
   const __bf16* W;       // [E, N, d]
-  const int32_t* idx;    // [T, k]; ids outside [0, E) add nothing
-  const float* topk_w;   // [T, k]
+  int32_t* idx;          // [T, k]; ids outside [0, E) add nothing (written when plog is set)
+  float* topk_w;         // [T, k] (written when plog is set)
   __bf16* out;           // [T, N] or null
   const int64_t* slot = nullptr;
   long long num_slots = 0;
   __bf16* cache = nullptr;
   int T, d, N, E, k;
+  // Set: the routing is selected in the kernel from the small-T router's
+  // class partials (launch_router_partial; Tp rows per class plane), with
+  // the selection bias and scale, instead of read from idx / topk_w.
+  const float* plog = nullptr;
+  int Tp = 0;
+  const float* bias = nullptr;
+  float scale = 1.f;
 };
 int decode_token_stages(int T, int d, int N, int E, int k);
 hipError_t launch_decode_token(const DecodeTokenArgs& a, int stages, hipStream_t stream);

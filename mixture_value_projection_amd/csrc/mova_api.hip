@@ -447,21 +447,32 @@ static int value_forward_impl(const void* x, const void* router_w, const float* 
 
   const Path path = choose_path(T, k);
   const bool grouped = path == Path::Grouped;
+  const int tok_stages = grouped ? 0 : decode_token_stages(T, d, N, E, k);
   hipError_t err = hipSuccess;
   if (given == nullptr) {
     StageScope sc(0, stream);
     RouterArgs ra{xb, (const __bf16*)router_w, router_b, T, d, E, k, scale, idx, w,
                   grouped ? chunk : nullptr};
-    err = grouped ? launch_router_lds(ra, stream) : launch_router_small(ra, plog, stream);
+    // The token-major kernel selects for its token itself from the partials.
+    err = grouped      ? launch_router_lds(ra, stream)
+          : tok_stages ? launch_router_partial(ra, plog, stream)
+                       : launch_router_small(ra, plog, stream);
   }
   if (err != hipSuccess) return MOVA_ERR_HIP;
 
   if (path == Path::Decode) {
     StageScope sc(2, stream);
-    if (const int stages = decode_token_stages(T, d, N, E, k)) {
-      // Token-major kernel: the k-way combine is fused into it.
+    if (const int stages = tok_stages) {
+      // Token-major kernel: the top-k selection (router's partials) and the
+      // k-way combine are fused into it.
       DecodeTokenArgs ta{xb, wb, idx, w, (__bf16*)out};
       ta.T = T; ta.d = d; ta.N = N; ta.E = E; ta.k = k;
+      if (given == nullptr) {
+        ta.plog = plog;
+        ta.Tp = ceil_div(T, 16) * 16;
+        ta.bias = router_b;
+        ta.scale = scale;
+      }
       if (pg != nullptr) {
         ta.slot = pg->slot;
         ta.num_slots = (long long)pg->num_blocks * pg->block_size;
