@@ -273,6 +273,20 @@ def test_workload_full(name):
     say(f"  {st}")
 
 
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16])
+def test_small_batch_full_size(T):
+    """Small-batch decode at the value layer's full size (the token-major
+    kernel with the selection and the combine fused, T * k <= 64): every
+    token against the oracle."""
+    sh = inputs.WORKLOADS["decode"].shape
+    say(f"small batch T={T}: full parity")
+    g = workload_inputs("decode", T=T)
+    out, idx, w = run_forward(g, sh.k, sh.scale, sh.n_kv_heads, sh.head_dim)
+    st = P.full_check(g, sh.k, sh.scale, sh.n_kv_heads, sh.head_dim, out, idx, w,
+                      what=f"small batch T={T}")
+    say(f"  {st}")
+
+
 def sample_rows(T, n, seed, extra=()):
     rng = np.random.default_rng(seed)
     rows = set(rng.choice(T, size=min(n, T), replace=False).tolist())
