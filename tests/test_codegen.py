@@ -41,3 +41,33 @@ def test_no_scratch(asm):
                                   "ffn.hip"])
 def test_contractions_use_mfma(asm, name):
     assert re.search(r"\bv_mfma_f32_16x16x32_bf16\b", asm[name])
+
+
+def _bodies(text, prefix):
+    """Assembly bodies of the kernels whose mangled names start with prefix."""
+    lines = text.splitlines()
+    out = []
+    for i, line in enumerate(lines):
+        if re.match(rf"^{prefix}\w*:", line):
+            j = i
+            while j < len(lines) and ".end_amdhsa_kernel" not in lines[j]:
+                j += 1
+            out.append((line.split(":")[0], lines[i:j]))
+    return out
+
+
+@pytest.mark.parametrize("name,prefix", [("router.hip", "_ZN4mova17router_lds_kernel"),
+                                         ("decode.hip", "_ZN4mova19decode_token_kernel")])
+def test_direct_load_rings_stay_in_flight(asm, name, prefix):
+    """Fragment reads of the direct-load rings do not wait for every
+    outstanding load (a vmcnt(0) right before a ds_read would drain the ring);
+    the counter waits the kernels set themselves keep later chunks in flight."""
+    bodies = _bodies(asm[name], prefix)
+    assert bodies, prefix
+    for kname, body in bodies:
+        ins = [l.strip() for l in body if l.strip() and not l.strip().startswith((";", "."))]
+        for a, b in zip(ins, ins[1:]):
+            assert not (re.match(r"s_waitcnt vmcnt\(0\)$", a) and b.startswith("ds_read_b128")), kname
+        partial = [l for l in ins if re.match(r"s_waitcnt vmcnt\(([1-9]\d*)\)", l)]
+        if "Li2ELi4EEEv" not in kname:  # the 2-stage ring keeps nothing in flight at its wait
+            assert partial, f"{kname}: no partial counter wait"
