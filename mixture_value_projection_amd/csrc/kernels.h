@@ -66,6 +66,9 @@ int router_small_plog_floats(int T);
 hipError_t launch_router_small(const RouterArgs& a, float* plog, hipStream_t stream);
 // Its first kernel alone (the class partials, for a consumer that selects).
 hipError_t launch_router_partial(const RouterArgs& a, float* plog, hipStream_t stream);
+// The same partials for up to 128 experts (the FFN router): plog rows of 128
+// floats, 4 * ceil(T / 16) * 16 rows.
+hipError_t launch_router_partial_wide(const RouterArgs& a, float* plog, hipStream_t stream);
 
 // Experts the dispatch kernels handle (the value router itself takes at most
 // kMaxExperts; routing of wider layers comes from their own router).

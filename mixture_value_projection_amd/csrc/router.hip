@@ -275,11 +275,12 @@ hipError_t launch_router_lds_wide(const RouterArgs& a, hipStream_t stream) {
 // Block (g, eb, rc) computes the class-rc partial logits of token group g (16
 // tokens) against expert block eb (16 experts), all of its loads issued before
 // its MFMAs.  The top-k kernel adds the four class partials in class order and
-// selects with one wave per token.
+// selects with one wave per token.  plog rows are ld floats apart (64 for the
+// value experts, 128 for the FFN's up to 128 experts).
 template <int U>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void router_partial_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, int T, int d, int E,
-    float* __restrict__ plog /* [4][Tp][64] */, int Tp) {
+    float* __restrict__ plog /* [4][Tp][ld] */, int Tp, int ld) {
   const int g = blockIdx.x, eb = blockIdx.y, rc = blockIdx.z;
   const int lane = threadIdx.x, q = lane >> 4, r16 = lane & 15;
   const bf16_t* xrow = x + (size_t)min(g * 16 + r16, T - 1) * d + q * 8;
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    plog[((size_t)rc * Tp + g * 16 + q * 4 + i) * kMaxExperts + eb * 16 + r16] = acc[i];
+    plog[((size_t)rc * Tp + g * 16 + q * 4 + i) * ld + eb * 16 + r16] = acc[i];
 }
 
 __global__ __launch_bounds__(256) void router_topk_kernel(
@@ -331,7 +332,16 @@ int router_small_plog_floats(int T) { return 4 * ceil_div(T, 16) * 16 * kMaxExpe
 
 hipError_t launch_router_partial(const RouterArgs& a, float* plog, hipStream_t stream) {
   const int G = ceil_div(a.T, 16);
-  router_partial_kernel<20><<<dim3(G, 4, 4), 64, 0, stream>>>(a.x, a.wr, a.T, a.d, a.E, plog, G * 16);
+  router_partial_kernel<20><<<dim3(G, 4, 4), 64, 0, stream>>>(a.x, a.wr, a.T, a.d, a.E, plog, G * 16,
+                                                             kMaxExperts);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_partial_wide(const RouterArgs& a, float* plog, hipStream_t stream) {
+  if (a.E > kMaxDispatchExperts) return hipErrorInvalidValue;
+  const int G = ceil_div(a.T, 16);
+  router_partial_kernel<20><<<dim3(G, ceil_div(a.E, 16), 4), 64, 0, stream>>>(
+      a.x, a.wr, a.T, a.d, a.E, plog, G * 16, kMaxDispatchExperts);
   return hipGetLastError();
 }
 

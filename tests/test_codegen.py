@@ -6,8 +6,8 @@ assembly, runs nothing).
   MFMA results between register files at loop heads produced stale values on
   the GPU.
 * No scratch (private segment) use: nothing spills.
-* Every file whose kernels contract issues MFMA (router, grouped GEMM,
-  decode, dense projection, FFN router).
+* Every file whose kernels contract issues MFMA (routers, grouped GEMM,
+  decode, dense projection).
 """
 import concurrent.futures
 import re
@@ -37,8 +37,7 @@ def test_no_scratch(asm):
     assert any(re.search(r"\.private_segment_fixed_size", t) for t in asm.values())
 
 
-@pytest.mark.parametrize("name", ["router.hip", "grouped_gemm.hip", "decode.hip", "dense.hip",
-                                  "ffn.hip"])
+@pytest.mark.parametrize("name", ["router.hip", "grouped_gemm.hip", "decode.hip", "dense.hip"])
 def test_contractions_use_mfma(asm, name):
     assert re.search(r"\bv_mfma_f32_16x16x32_bf16\b", asm[name])
 
