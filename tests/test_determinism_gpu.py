@@ -56,11 +56,11 @@ def test_route_chunking_bitwise(T, chunk):
         assert torch.equal(idx[c0:c0 + chunk], i2) and torch.equal(w[c0:c0 + chunk], w2)
 
 
-@pytest.mark.parametrize("T", [64, 1000])
+@pytest.mark.parametrize("T", [4, 64, 1000])
 def test_graph_replay_matches_eager(T):
     """A captured call replays to the eager result every time, with eager work
-    and synchronisations between the replays (decode path at T=64, grouped
-    path at T=1000)."""
+    and synchronisations between the replays (token-major kernel with the
+    selection fused at T=4, decode path at T=64, grouped path at T=1000)."""
     g = gpu_layer(T, seed=3)
     ws = torch.empty(binding.workspace_bytes(T, 2560, 64, 4, 8, 128), dtype=torch.uint8, device=DEV)
     eager = fwd_ws(g, ws).clone()
@@ -224,3 +224,28 @@ def test_decode_chain_kernel_bitwise(T, d, E, k, heads, hd):
         assert torch.equal(a, c), f"{name}: chain kernel differs from the grouped path"
         assert torch.equal(b, c), f"{name}: decode kernel differs from the grouped path"
         assert torch.equal(e, c), f"{name}: token-major kernel differs from the grouped path"
+
+
+@pytest.mark.parametrize("Ts", [(4, 64), (64, 1000), (1000, 2048)])
+def test_concurrent_streams_bitwise(Ts):
+    """Two calls in flight at once on two streams, each with its own
+    workspace and output (different paths where the token counts differ),
+    give the bits of the same calls made alone."""
+    gs = [gpu_layer(T, seed=20 + i) for i, T in enumerate(Ts)]
+    wss = [torch.empty(binding.workspace_bytes(T, 2560, 64, 4, 8, 128), dtype=torch.uint8, device=DEV)
+           for T in Ts]
+    refs = [fwd_ws(g, ws).clone() for g, ws in zip(gs, wss)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in Ts]
+    outs = [torch.empty_like(r) for r in refs]
+    print(f"two streams T={Ts}", flush=True)
+    for rep in range(10):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        for g, ws, o, s in zip(gs, wss, outs, streams):
+            with torch.cuda.stream(s):
+                fwd_ws(g, ws, o)
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outs, refs)):
+            assert torch.equal(o, r), f"rep {rep}: stream {i} (T={Ts[i]}) differs"
