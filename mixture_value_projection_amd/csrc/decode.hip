@@ -424,9 +424,10 @@ template <int kSW, int kS>
 static int tok_smem(int d) { return kTokHeader + 4 * (tok_x_bytes(d) + kS * kSW * kTokSlot); }
 
 // kRoute: the routing comes as the small-T router's class partials (plog, Tp
-// rows per class plane); wave 0 of each workgroup adds them in class order and
-// selects its token's top k with topk_tokens, the router's own selection, and
-// the workgroups of column group 0 also write the routing to idx / topk_w.
+// rows per class plane); every wave adds them in class order and selects the
+// token's top k with topk_tokens, the router's own selection (so each wave
+// starts its weight loads without waiting for another), and wave 0 of the
+// workgroups of column group 0 also writes the routing to idx / topk_w.
 template <int kSW, int kS, bool kRoute>  // kSW: slots per wave (k <= 4 * kSW); kS: ring stages
 __global__ __launch_bounds__(256) void decode_token_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int32_t* __restrict__ idx,
@@ -462,29 +463,43 @@ __global__ __launch_bounds__(256) void decode_token_kernel(
     __builtin_amdgcn_global_load_lds((const void*)(xrow + min(i * 512 + lane * 8, d - 8)),
                                      (lds_void*)(region + i * 1024), 16, 0, 0);
 
+  // This wave's slots' expert ids and weights.
+  int rs_e[kSW];
+  float rs_w[kSW];
   if constexpr (kRoute) {
-    if (wave == 0) {
-      const size_t cls = (size_t)Tp * kMaxExperts;
-      const float* src = plog + (size_t)t * kMaxExperts + lane;
-      const float lg[1] = {((src[0] + src[cls]) + src[2 * cls]) + src[3 * cls]};
-      const float b_lane = (bias != nullptr && lane < E) ? bias[lane] : 0.f;
-      int my_idx[1];
-      float my_w[1];
-      topk_tokens<1>(lg, b_lane, lane, E, k, scale, my_idx, my_w);
-      if (lane < k) {
-        sh_e[lane] = my_idx[0];
-        sh_w[lane] = my_w[0];
-        if (n0 == 0) {
-          idx[(size_t)t * k + lane] = my_idx[0];
-          topk_w[(size_t)t * k + lane] = my_w[0];
-        }
+    const size_t cls = (size_t)Tp * kMaxExperts;
+    const float* srcp = plog + (size_t)t * kMaxExperts + lane;
+    const float lg[1] = {((srcp[0] + srcp[cls]) + srcp[2 * cls]) + srcp[3 * cls]};
+    const float b_lane = (bias != nullptr && lane < E) ? bias[lane] : 0.f;
+    int my_idx[1];
+    float my_w[1];
+    topk_tokens<1>(lg, b_lane, lane, E, k, scale, my_idx, my_w);
+#pragma unroll
+    for (int s2 = 0; s2 < kSW; ++s2) {
+      const int j = wave + 4 * s2;
+      rs_e[s2] = j < k ? __builtin_amdgcn_readlane(my_idx[0], j) : -1;
+      rs_w[s2] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w[0]), j & 63));
+    }
+    if (wave == 0 && lane < k) {  // the ids for the combine below
+      sh_e[lane] = my_idx[0];
+      if (n0 == 0) {
+        idx[(size_t)t * k + lane] = my_idx[0];
+        topk_w[(size_t)t * k + lane] = my_w[0];
       }
     }
-  } else if (tid < k) {
-    sh_e[tid] = idx[(size_t)t * k + tid];
-    sh_w[tid] = topk_w[(size_t)t * k + tid];
+  } else {
+    if (tid < k) {
+      sh_e[tid] = idx[(size_t)t * k + tid];
+      sh_w[tid] = topk_w[(size_t)t * k + tid];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s2 = 0; s2 < kSW; ++s2) {
+      const int j = wave + 4 * s2;
+      rs_e[s2] = j < k ? sh_e[j] : -1;
+      rs_w[s2] = j < k ? sh_w[j] : 0.f;
+    }
   }
-  __syncthreads();
 
   // This wave's slots and the source of its lane in each direct load: load
   // i of slot s covers rows 4i .. 4i + 3, the lane's row 4i + lane / 16 and
@@ -501,7 +516,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(
 #pragma unroll
   for (int s = 0; s < kSW; ++s) {
     sj[s] = wave + 4 * s;
-    const int e = sj[s] < k ? sh_e[sj[s]] : -1;
+    const int e = rs_e[s];
     valid[s] = e >= 0 && e < E;
     const int ee = valid[s] ? e : 0;
 #pragma unroll
@@ -552,7 +567,7 @@ __global__ __launch_bounds__(256) void decode_token_kernel(
   if (lane < 16) {
 #pragma unroll
     for (int s = 0; s < kSW; ++s)
-      if (valid[s]) sh_p[sj[s] * 16 + lane] = (f16_t)(sh_w[sj[s]] * siluf(acc[s][0]));
+      if (valid[s]) sh_p[sj[s] * 16 + lane] = (f16_t)(rs_w[s] * siluf(acc[s][0]));
   }
   __syncthreads();
   if (tid < 16) {
