@@ -73,9 +73,30 @@ def build_library(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIBPATH)
+    build_example()
     if verbose:
         print(f"built {LIBPATH}")
     return LIBPATH
+
+
+EXAMPLE_SRC = os.path.join(ROOT, "examples", "value_forward.c")
+EXAMPLE = os.path.join(LIBDIR, "mova_value_forward_example")
+CLANG = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "llvm", "bin", "clang")
+
+
+def build_example() -> str:
+    """Compile examples/value_forward.c (a plain C caller of the C ABI) next to
+    the library, which it finds through its rpath."""
+    clang = CLANG if os.path.exists(CLANG) else "/opt/rocm/llvm/bin/clang"
+    rocm = os.path.realpath(os.path.join(os.path.dirname(os.path.realpath(HIPCC)), ".."))
+    cmd = [clang, "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), EXAMPLE_SRC, "-o", EXAMPLE, f"-L{LIBDIR}", "-lmova",
+           f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"example build failed:\n{r.stdout}\n{r.stderr}")
+    return EXAMPLE
 
 
 if __name__ == "__main__":

@@ -337,3 +337,12 @@ def test_record_entry_points_reject_on_the_host(lib):
     assert fwd_rec(ids=None) == INVALID and from_rec(w=None) == INVALID
     assert fwd_rec(ids=FAKE + 2) == INVALID and from_rec(w=FAKE + 1) == INVALID
     assert from_rec(ws=None) == WORKSPACE
+
+
+def test_c_example_is_built():
+    """build() compiles the plain-C example caller of the C ABI next to the
+    library (it runs in the GPU tests)."""
+    from mixture_value_projection_amd import build
+    assert os.path.exists(build.EXAMPLE)
+    with open(build.EXAMPLE, "rb") as fh:
+        assert fh.read(4) == b"\x7fELF"
