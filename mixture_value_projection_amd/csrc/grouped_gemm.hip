@@ -204,6 +204,78 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[kBM / kWM / 16][kBN / kWN 
   }
 }
 
+// The same k step with the next step's direct loads issued among the first
+// sub-step's MFMAs, and the second sub-step's fragment reads among its last
+// ones (tiles of up to 256 rows, equal loads per wave).  Issued together at
+// the top of the step, the eight waves' loads reach the address unit as one
+// burst, and the waves queued behind it issue no MFMAs meanwhile; spread out,
+// they drain while the MFMAs run (measured: the dense T = 32768 GEMM 144-145
+// -> 138-141 us).  The load pointers advance in place by k_inc (0 in the last
+// step, which reloads its own k step into the unused stage and keeps the step
+// free of branches), so no address temporaries are held across the MFMAs.
+// The 352-row tile keeps mma_step: it has no registers to spare for this
+// schedule (it spills), and without the schedule it measured mixed.
+template <MOVA_TILE_PARAMS, int kUsed>
+__device__ __forceinline__ void mma_step_spread(f32x4 (&acc)[kBM / kWM / 16][kBN / kWN / 16],
+                                                const char* stage, int wm, int wn, int q, int r16,
+                                                TileCtx<MOVA_TILE_ARGS>& c, char* next, int wave,
+                                                int k_inc) {
+  using TL = Tile<MOVA_TILE_ARGS>;
+  static_assert(TL::kEvenA, "every wave issues the same loads");
+  constexpr int NJ = TL::kNJ;
+  constexpr int L = TL::kLoadsA + TL::kLoadsB;  // direct loads per wave and step
+  constexpr int M0 = kUsed * NJ;                // MFMAs per sub-step
+  constexpr int kPer = (M0 / 2) / L > 0 ? (M0 / 2) / L : 1;  // MFMAs before each load
+  constexpr int kRest = M0 - kPer * L;
+  constexpr int kR = kUsed + NJ;  // fragment reads per sub-step
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int chunk = ks * 4 + q;
+    Frag16 fa[kUsed], fb[NJ];
+#pragma unroll
+    for (int i = 0; i < kUsed; ++i) fa[i].u = load16(stage + swz(wm * TL::kRowsW + i * 16 + r16, chunk));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      fb[j].u = load16(stage + TL::kTileA + swz(wn * TL::kColsW + j * 16 + r16, chunk));
+#pragma unroll
+    for (int i = 0; i < kUsed; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(fa[i].h, fb[j].h, acc[i][j]);
+    if (ks == 0) {
+#pragma unroll
+      for (int i = 0; i < TL::kLoadsA; ++i) {
+        c.a_src[i] += k_inc;
+        __builtin_amdgcn_global_load_lds((const void*)c.a_src[i],
+                                         (lds_void*)(next + (wave * TL::kLoadsA + i) * 1024), 16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < TL::kLoadsB; ++i) {
+        c.b_src[i] += k_inc;
+        __builtin_amdgcn_global_load_lds((const void*)c.b_src[i],
+                                         (lds_void*)(next + TL::kTileA + (wave * TL::kLoadsB + i) * 1024),
+                                         16, 0, 0);
+      }
+    }
+  }
+  // Order (sched_group_barrier masks: 0x100 LDS reads, 0x008 MFMA, 0x020
+  // vector-memory reads): sub-step 0's reads; its first MFMAs with one load
+  // after every kPer of them; its remaining MFMAs with sub-step 1's reads in
+  // two halves among them; sub-step 1's MFMAs.  The closing sched_barrier
+  // keeps the caller's wait and barrier after every MFMA of the step.
+  __builtin_amdgcn_sched_group_barrier(0x100, kR, 0);
+#pragma unroll
+  for (int n = 0; n < L; ++n) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kRest / 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kR / 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, kRest - kRest / 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kR - kR / 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, M0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 constexpr bool mode_routed(int m) {
   return m == kGemmRoutedSilu || m == kGemmRoutedSwiGLU || m == kGemmRoutedLinear;
 }
@@ -328,10 +400,14 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     auto steps = [&](auto used) {
       for (int kt = 0; kt < KT; ++kt) {
         char* cur = smem + (kt & 1) * TL::kStage;
-        if (kt + 1 < KT)
-          issue_loads<MOVA_TILE_ARGS>(c, smem + ((kt + 1) & 1) * TL::kStage, wave,
-                                      (kt + 1) * kRowBytes);
-        mma_step<MOVA_TILE_ARGS, decltype(used)::value>(acc, cur, wm, wn, q, r16);
+        char* nxt = smem + ((kt + 1) & 1) * TL::kStage;
+        if constexpr (kBM <= 256) {
+          mma_step_spread<MOVA_TILE_ARGS, decltype(used)::value>(acc, cur, wm, wn, q, r16, c, nxt, wave,
+                                                                 kt + 1 < KT ? kRowBytes : 0);
+        } else {
+          if (kt + 1 < KT) issue_loads<MOVA_TILE_ARGS>(c, nxt, wave, (kt + 1) * kRowBytes);
+          mma_step<MOVA_TILE_ARGS, decltype(used)::value>(acc, cur, wm, wn, q, r16);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
