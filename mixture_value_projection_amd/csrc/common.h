@@ -26,6 +26,18 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// The same load with the non-temporal hint, for data read once per call (the
+// decode kernels' expert weights): it keeps the stream from displacing what
+// the caches hold for reuse.  Measured on the decode step at T = 64 (weights
+// rotated over 4 copies): weight stream 60.4 -> 53.5 us.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Cache-policy operand of a direct-to-LDS load (global_load_lds) with the
+// non-temporal bit set.
+constexpr int kLdsLoadNonTemporal = 2;
+
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }

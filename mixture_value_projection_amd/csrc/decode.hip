@@ -19,7 +19,10 @@
 // grid).  With 4-step batches and one row group, the weights are loaded as
 // whole 256-byte row segments (16 lanes per row, which the vector cache
 // serves with far fewer requests than 16 rows per 16 lanes) and turned into
-// fragments through a small LDS scratch of the wave's own.  The k loop runs in batches of kUnroll steps over a ring of three
+// fragments through a small LDS scratch of the wave's own; these loads carry
+// the non-temporal hint (the weights are read once per call; measured at
+// T = 64: 60.4 -> 53.5 us, while on the fragment loads of the other layouts
+// the hint was slower, T = 128 81 -> 92 us).  The k loop runs in batches of kUnroll steps over a ring of three
 // register buffers, so three batches of loads are in flight while a batch's
 // MFMAs run; the waves never wait for each other inside the loop.  The first
 // two weight batches are issued before the routing scan, which they do not
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int g = 0; g < kGroups; ++g) {
       if constexpr (kRowLoads) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[g][i].u = load16(wseg[g][i] + (size_t)bt * 128);
+        for (int i = 0; i < 4; ++i) b[g][i].u = load16_stream(wseg[g][i] + (size_t)bt * 128);
       } else {
         const bf16_t* p = wrow[g] + (size_t)bt * kUnroll * 32;
 #pragma unroll
@@ -428,7 +431,9 @@ static int tok_smem(int d) { return kTokHeader + 4 * (tok_x_bytes(d) + kS * kSW 
 // token's top k with topk_tokens, the router's own selection (so each wave
 // starts its weight loads without waiting for another), and wave 0 of the
 // workgroups of column group 0 also writes the routing to idx / topk_w.
-template <int kSW, int kS, bool kRoute>  // kSW: slots per wave (k <= 4 * kSW); kS: ring stages
+// kNt: the weight loads carry the non-temporal hint (chosen by T, see
+// token_nontemporal).
+template <int kSW, int kS, bool kRoute, bool kNt>  // kSW: slots per wave (k <= 4 * kSW); kS: ring stages
 __global__ __launch_bounds__(256) void decode_token_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W, int32_t* __restrict__ idx,
     float* __restrict__ topk_w, const float* __restrict__ plog, int Tp,
@@ -530,7 +535,8 @@ __global__ __launch_bounds__(256) void decode_token_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(src[s][i] + min(j * 128 + off[i], d - 8)),
-                                         (lds_void*)(stage + s * kTokSlot + i * 1024), 16, 0, 0);
+                                         (lds_void*)(stage + s * kTokSlot + i * 1024), 16, 0,
+                                         kNt ? kLdsLoadNonTemporal : 0);
   };
 
   f32x4 acc[kSW];
@@ -613,15 +619,25 @@ int decode_token_stages(int T, int d, int N, int E, int k) {
   return tok_smem<1, 3>(d) <= 160 * 1024 ? 3 : 0;
 }
 
-template <int kSW, int kS>
-static hipError_t launch_token_cfg(const DecodeTokenArgs& a, hipStream_t stream) {
-  auto kern = a.plog != nullptr ? decode_token_kernel<kSW, kS, true> : decode_token_kernel<kSW, kS, false>;
+// Whether the token kernel's weight loads take the non-temporal hint.
+// Measured on the value experts (k = 4, graph replay, weights rotated over 4
+// copies), call time in us without / with it:
+//   T        1      2      4      6      8      12     16
+//   plain    13.69  14.86  19.40  27.41  32.14  47.65  52.87
+//   hint     13.95  15.30  18.96  26.39  30.12  46.70  54.25
+// so it is taken for T = 3 .. 12 at k <= 4 (other k: not measured, plain).
+static bool token_nontemporal(const DecodeTokenArgs& a) { return a.k <= 4 && a.T >= 3 && a.T <= 12; }
+
+template <int kSW, int kS, bool kNt>
+static hipError_t launch_token_nt(const DecodeTokenArgs& a, hipStream_t stream) {
+  auto kern = a.plog != nullptr ? decode_token_kernel<kSW, kS, true, kNt>
+                                : decode_token_kernel<kSW, kS, false, kNt>;
   const int smem = tok_smem<kSW, kS>(a.d);
   static std::atomic<unsigned long long> attr_done{0};
   hipError_t err = once_per_device(attr_done, [&]() {
-    hipError_t e1 = hipFuncSetAttribute((const void*)decode_token_kernel<kSW, kS, true>,
+    hipError_t e1 = hipFuncSetAttribute((const void*)decode_token_kernel<kSW, kS, true, kNt>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    hipError_t e2 = hipFuncSetAttribute((const void*)decode_token_kernel<kSW, kS, false>,
+    hipError_t e2 = hipFuncSetAttribute((const void*)decode_token_kernel<kSW, kS, false, kNt>,
                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     return e1 != hipSuccess ? e1 : e2;
   });
@@ -630,6 +646,12 @@ static hipError_t launch_token_cfg(const DecodeTokenArgs& a, hipStream_t stream)
       a.x, a.W, a.idx, a.topk_w, a.plog, a.Tp, a.bias, a.scale, a.out, a.slot, a.num_slots,
       a.cache, a.T, a.d, a.N, a.E, a.k);
   return hipGetLastError();
+}
+
+template <int kSW, int kS>
+static hipError_t launch_token_cfg(const DecodeTokenArgs& a, hipStream_t stream) {
+  return token_nontemporal(a) ? launch_token_nt<kSW, kS, true>(a, stream)
+                              : launch_token_nt<kSW, kS, false>(a, stream);
 }
 
 hipError_t launch_decode_token(const DecodeTokenArgs& a, int stages, hipStream_t stream) {

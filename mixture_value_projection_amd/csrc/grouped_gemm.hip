@@ -162,8 +162,8 @@ struct TileCtx {
 };
 
 // Direct loads of one k step: A block j (rows 8j .. 8j+7) for j = wave * kLoadsA + i,
-// B block j for j = wave * kLoadsB + i.
-template <MOVA_TILE_PARAMS>
+// B block j for j = wave * kLoadsB + i; kAuxB is the B loads' cache policy.
+template <MOVA_TILE_PARAMS, int kAuxB = 0>
 __device__ __forceinline__ void issue_loads(const TileCtx<MOVA_TILE_ARGS>& c, char* stage, int wave,
                                             int k_byte) {
   using TL = Tile<MOVA_TILE_ARGS>;
@@ -177,7 +177,7 @@ __device__ __forceinline__ void issue_loads(const TileCtx<MOVA_TILE_ARGS>& c, ch
   for (int i = 0; i < TL::kLoadsB; ++i)
     __builtin_amdgcn_global_load_lds((const void*)(c.b_src[i] + k_byte),
                                      (lds_void*)(stage + TL::kTileA + (wave * TL::kLoadsB + i) * 1024),
-                                     16, 0, 0);
+                                     16, 0, kAuxB);
 }
 
 // One k step (two 32-wide MFMA steps) of the wave's sub-tile, for its first
@@ -296,7 +296,10 @@ constexpr bool mode_swiglu(int m) { return m == kGemmRoutedSwiGLU || m == kGemmD
 // are gate rows 16b .. 16b+15 and rows 32b+16 .. 32b+31 the matching up rows,
 // so the wave's column tiles 2j and 2j+1 hold the gate and up values of the
 // same 16 outputs c = (column of tile 2j) / 2 .. + 15; out has N / 2 columns.
-template <MOVA_TILE_PARAMS, int kMode>
+//
+// kNtB: the weight (B) loads carry the non-temporal hint, for calls where
+// each expert's weight tile is read by a single row tile (launch_routed_mode).
+template <MOVA_TILE_PARAMS, int kMode, bool kNtB = false>
 __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ W,
     const int32_t* __restrict__ perm, const float* __restrict__ topk_w,
@@ -307,6 +310,8 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
   constexpr int WN = TL::kColsW;  // columns per wave
   static_assert(!mode_swiglu(kMode) || WN % 32 == 0, "SwiGLU pairs 16-column tiles");
   static_assert(TL::kEvenA || kS == 2, "the ring's wait counts assume equal loads per wave");
+  static_assert(!kNtB || (kBM > 256 && kS == 2), "the hint is wired into the 2-stage mma_step loop only");
+  constexpr int kAuxB = kNtB ? kLdsLoadNonTemporal : 0;
   extern __shared__ __attribute__((aligned(1024))) char smem[];  // kS stages
   __shared__ int tile_pair[kDense ? 1 : kBM];
   __shared__ float tile_w[kDense ? 1 : kBM];
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
   const int nv = min(TL::kMI, max(0, ceil_div(rows - wm * TL::kRowsW, 16)));
   const bool active = nv > 0;
   if constexpr (kS == 2) {
-    issue_loads<MOVA_TILE_ARGS>(c, smem, wave, 0);
+    issue_loads<MOVA_TILE_ARGS, kAuxB>(c, smem, wave, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // A wave whose valid rows fit in the first half of its row blocks runs
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
           mma_step_spread<MOVA_TILE_ARGS, decltype(used)::value>(acc, cur, wm, wn, q, r16, c, nxt, wave,
                                                                  kt + 1 < KT ? kRowBytes : 0);
         } else {
-          if (kt + 1 < KT) issue_loads<MOVA_TILE_ARGS>(c, nxt, wave, (kt + 1) * kRowBytes);
+          if (kt + 1 < KT) issue_loads<MOVA_TILE_ARGS, kAuxB>(c, nxt, wave, (kt + 1) * kRowBytes);
           mma_step<MOVA_TILE_ARGS, decltype(used)::value>(acc, cur, wm, wn, q, r16);
         }
         __builtin_amdgcn_s_waitcnt(0);
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
     } else {
       for (int kt = 0; kt < KT; ++kt) {
         if (kt + 1 < KT)
-          issue_loads<MOVA_TILE_ARGS>(c, smem + ((kt + 1) & 1) * TL::kStage, wave,
+          issue_loads<MOVA_TILE_ARGS, kAuxB>(c, smem + ((kt + 1) & 1) * TL::kStage, wave,
                                       (kt + 1) * kRowBytes);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -500,9 +505,9 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
   }
 }
 
-template <MOVA_TILE_PARAMS, int kMode>
+template <MOVA_TILE_PARAMS, int kMode, bool kNtB = false>
 hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) {
-  auto kern = gemm_kernel<MOVA_TILE_ARGS, kMode>;
+  auto kern = gemm_kernel<MOVA_TILE_ARGS, kMode, kNtB>;
   constexpr int smem = kS * Tile<MOVA_TILE_ARGS>::kStage;
   constexpr int threads = Tile<MOVA_TILE_ARGS>::kThreads;
   static std::atomic<unsigned long long> attr_done{0};
@@ -520,7 +525,18 @@ hipError_t launch_tiles(const GemmArgs& a, long long tiles, hipStream_t stream) 
 template <int kMode>
 static hipError_t launch_routed_mode(const GemmArgs& a, long long ub, hipStream_t stream) {
   const GemmTile t = a.tile;
-  if (t.bm == 352 && t.bn == 256) return launch_tiles<352, 256, 2, 4, 2, kMode>(a, ub, stream);
+  if (t.bm == 352 && t.bn == 256) {
+    // Value experts whose rows fit one 352-row tile (the busiest expert
+    // holds about 1.3 R rows, R = T k / E) read each weight tile once:
+    // the weight loads then take the non-temporal hint.  Measured at
+    // prefill T = 4096 (R = 256): 146-147 -> 141 us; with several row tiles
+    // per expert (chunked R = 512, skewed R = 2048) the hint was 1 % slower.
+    if constexpr (kMode == kGemmRoutedSilu) {
+      const long long R = ((long long)a.T * a.k + a.E / 2) / a.E;
+      if (R * 13 <= 352 * 10) return launch_tiles<352, 256, 2, 4, 2, kMode, true>(a, ub, stream);
+    }
+    return launch_tiles<352, 256, 2, 4, 2, kMode>(a, ub, stream);
+  }
   if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, kMode>(a, ub, stream);
   if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, kMode>(a, ub, stream);
   if (t.bm == 128 && t.bn == 128 && t.waves == 8) {

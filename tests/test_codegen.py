@@ -8,6 +8,7 @@ assembly, runs nothing).
 * No scratch (private segment) use: nothing spills.
 * Every file whose kernels contract issues MFMA (routers, grouped GEMM,
   decode, dense projection).
+* The decode kernels' stream-once weight loads carry the non-temporal hint.
 """
 import concurrent.futures
 import re
@@ -70,3 +71,16 @@ def test_direct_load_rings_stay_in_flight(asm, name, prefix):
         partial = [l for l in ins if re.match(r"s_waitcnt vmcnt\(([1-9]\d*)\)", l)]
         if "Li2ELi4EEEv" not in kname:  # the 2-stage ring keeps nothing in flight at its wait
             assert partial, f"{kname}: no partial counter wait"
+
+
+def test_decode_weight_stream_is_non_temporal(asm):
+    """The weight-streaming decode kernel's row-segment loads and the
+    token-major kernel's direct loads (its variant with the hint) are
+    non-temporal; the token rows, read by many workgroups, are not."""
+    text = asm["decode.hip"]
+    stream = [b for n, b in _bodies(text, "_ZN4mova13decode_kernel")]
+    assert stream and any(re.search(r"global_load_dwordx4 .* nt\b", l) for b in stream for l in b)
+    tok = _bodies(text, "_ZN4mova19decode_token_kernel")
+    hinted = [n for n, b in tok if any(re.search(r"global_load_lds_dwordx4 .* nt\b", l) for l in b)]
+    plain = [n for n, b in tok if not any(re.search(r"global_load_lds_dwordx4 .* nt\b", l) for l in b)]
+    assert hinted and plain, (len(hinted), len(plain))
