@@ -56,8 +56,9 @@ namespace mova {
 
 // kUnroll: k steps per batch; it divides the step count d / 32 (4 when it
 // can, else 2, which always does since d % 64 == 0).  kPair32: experts with
-// more than 16 pairs use 32-pair passes (worth it beyond 64 tokens; without
-// it the kernel holds fewer registers, and such experts take 16-pair passes).
+// more than 16 pairs use 32-pair passes (worth it once the experts average
+// more than 10 pairs; without it the kernel holds fewer registers and uses
+// the row-segment loads, and such experts take 16-pair passes).
 //
 // kMode selects the epilogue, as in the grouped GEMM (GemmMode):
 //   kGemmRoutedSilu    partial[pair, n] = fp16(w * SiLU(z))     (value experts)
@@ -727,7 +728,13 @@ static hipError_t launch_decode_mode(const DecodeArgs& a, hipStream_t stream) {
   narrow = narrow && kMode != kGemmRoutedSwiGLU;
   const dim3 grid(a.E * ceil_div(a.N, narrow ? 64 : 128));
   const bool unroll4 = (a.d / 32) % 4 == 0;
-  const bool pair32 = a.T > 64;
+  // 32-pair passes (fragment loads) once the experts average more than 10
+  // pairs; below, 16-pair passes with the non-temporal row-segment loads win
+  // even though an expert with more than 16 pairs reads its weights twice.
+  // Measured on the value experts (k = 4, E = 64), call times in us, 16- vs
+  // 32-pair passes: T = 96 64.3 vs 76.2, 128 79.4 vs 80.9, 160 81.5 vs 84.0,
+  // 192 98.0 vs 89.0, 256 105 vs 94.
+  const bool pair32 = (long long)a.T * a.k > 10LL * a.E;
   auto kern = narrow ? pick_decode_kernel<kMode, kMode == kGemmRoutedSwiGLU ? 2 : 1>(unroll4, pair32)
                      : pick_decode_kernel<kMode, 2>(unroll4, pair32);
   kern<<<grid, 256, 0, stream>>>(a.x, a.W, a.idx, a.topk_w, a.partial, (bf16_t*)a.out_h, a.T, a.d,

@@ -122,6 +122,8 @@ def _run(g, k, heads, hd, forced):
     (5, 512, 16, 8, 1, 64, "uniform"),
     (100, 512, 64, 1, 2, 128, "uniform"),
     (256, 512, 64, 4, 2, 128, "uniform"),
+    (160, 2560, 64, 4, 8, 128, "uniform"),   # 16-pair passes up to 10 pairs per expert on average
+    (150, 512, 64, 4, 2, 128, "one_expert"),  # ... and an expert of 150 pairs in ten of them
     (137, 512, 40, 6, 1, 128, "ties"),
     (256, 512, 64, 4, 1, 128, "one_expert"),
     (250, 1024, 7, 3, 1, 64, "one_expert"),
