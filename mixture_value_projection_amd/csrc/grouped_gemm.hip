@@ -215,7 +215,7 @@ __device__ __forceinline__ void mma_step(f32x4 (&acc)[kBM / kWM / 16][kBN / kWN 
 // free of branches), so no address temporaries are held across the MFMAs.
 // The 352-row tile keeps mma_step: it has no registers to spare for this
 // schedule (it spills), and without the schedule it measured mixed.
-template <MOVA_TILE_PARAMS, int kUsed>
+template <MOVA_TILE_PARAMS, int kUsed, int kAuxB = 0>
 __device__ __forceinline__ void mma_step_spread(f32x4 (&acc)[kBM / kWM / 16][kBN / kWN / 16],
                                                 const char* stage, int wm, int wn, int q, int r16,
                                                 TileCtx<MOVA_TILE_ARGS>& c, char* next, int wave,
@@ -253,7 +253,7 @@ __device__ __forceinline__ void mma_step_spread(f32x4 (&acc)[kBM / kWM / 16][kBN
         c.b_src[i] += k_inc;
         __builtin_amdgcn_global_load_lds((const void*)c.b_src[i],
                                          (lds_void*)(next + TL::kTileA + (wave * TL::kLoadsB + i) * 1024),
-                                         16, 0, 0);
+                                         16, 0, kAuxB);
       }
     }
   }
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
   constexpr int WN = TL::kColsW;  // columns per wave
   static_assert(!mode_swiglu(kMode) || WN % 32 == 0, "SwiGLU pairs 16-column tiles");
   static_assert(TL::kEvenA || kS == 2, "the ring's wait counts assume equal loads per wave");
-  static_assert(!kNtB || (kBM > 256 && kS == 2), "the hint is wired into the 2-stage mma_step loop only");
+  static_assert(!kNtB || kS == 2, "the hint is wired into the 2-stage loops only");
   constexpr int kAuxB = kNtB ? kLdsLoadNonTemporal : 0;
   extern __shared__ __attribute__((aligned(1024))) char smem[];  // kS stages
   __shared__ int tile_pair[kDense ? 1 : kBM];
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * kWM * kWN) void gemm_kernel(
         char* cur = smem + (kt & 1) * TL::kStage;
         char* nxt = smem + ((kt + 1) & 1) * TL::kStage;
         if constexpr (kBM <= 256) {
-          mma_step_spread<MOVA_TILE_ARGS, decltype(used)::value>(acc, cur, wm, wn, q, r16, c, nxt, wave,
+          mma_step_spread<MOVA_TILE_ARGS, decltype(used)::value, kAuxB>(acc, cur, wm, wn, q, r16, c, nxt, wave,
                                                                  kt + 1 < KT ? kRowBytes : 0);
         } else {
           if (kt + 1 < KT) issue_loads<MOVA_TILE_ARGS, kAuxB>(c, nxt, wave, (kt + 1) * kRowBytes);
@@ -528,14 +528,27 @@ static hipError_t launch_routed_mode(const GemmArgs& a, long long ub, hipStream_
   if (t.bm == 352 && t.bn == 256) {
     // Value experts whose rows fit one 352-row tile (the busiest expert
     // holds about 1.3 R rows, R = T k / E) read each weight tile once:
-    // the weight loads then take the non-temporal hint.  Measured at
-    // prefill T = 4096 (R = 256): 146-147 -> 141 us; with several row tiles
-    // per expert (chunked R = 512, skewed R = 2048) the hint was 1 % slower.
+    // the weight loads then take the non-temporal hint (measured below).
     if constexpr (kMode == kGemmRoutedSilu) {
       const long long R = ((long long)a.T * a.k + a.E / 2) / a.E;
       if (R * 13 <= 352 * 10) return launch_tiles<352, 256, 2, 4, 2, kMode, true>(a, ub, stream);
     }
     return launch_tiles<352, 256, 2, 4, 2, kMode>(a, ub, stream);
+  }
+  // The same for the 256- and 128-row tiles (2 stages).  Measured on the
+  // value layer (d = 2560, N = 1024, E = 64, graph replay), call times in us
+  // without / with the hint: T = 512 91 / 84, 1024 97 / 91, 1536 104 / 96,
+  // 2048 118 / 110, 3072 129 / 122, and with the 352-row tile T = 4096
+  // 146-147 / 141.  With several row tiles per expert (chunked R = 512,
+  // skewed R = 2048) it was about 1 % slower, and on the dense T = 32768
+  // GEMM, whose weight serves 128 row tiles, 14 % slower.
+  if constexpr (kMode == kGemmRoutedSilu) {
+    const long long R = ((long long)a.T * a.k + a.E / 2) / a.E;
+    if (R * 13 <= (long long)t.bm * 10) {
+      if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, kMode, true>(a, ub, stream);
+      if (t.bm == 128 && t.bn == 128 && t.waves == 8 && t.stages == 2)
+        return launch_tiles<128, 128, 2, 4, 2, kMode, true>(a, ub, stream);
+    }
   }
   if (t.bm == 256 && t.bn == 256) return launch_tiles<256, 256, 2, 4, 2, kMode>(a, ub, stream);
   if (t.bm == 128 && t.bn == 256) return launch_tiles<128, 256, 2, 4, 2, kMode>(a, ub, stream);
