@@ -604,7 +604,12 @@ __global__ __launch_bounds__(256) void decode_token_kernel(
 //   others     16.5  20.3  29.6  37.2  43.7  58.9  62.1  64.6  66.0
 //   4 stages   14.9  16.1  21.0  31.1  36.2  49.5  60.0  81.9  104.0
 //   3 stages   16.2  -     21.5  -     34.3  49.0  54.7  -     -
-// so it takes T * k <= 64, with 4 stages (84 KB of LDS, one workgroup per
+// and, once the weight-streaming kernel's row loads took the non-temporal
+// hint (one session, token-major vs streaming kernel):
+//   T          6     8     10    12    14    16
+//   token      26.2  30.0  42.5  46.2  50.0  52.7
+//   streaming  34.1  38.0  43.9  49.6  49.6  50.8
+// so it takes T * k <= 48, with 4 stages (84 KB of LDS, one workgroup per
 // CU) while its workgroups fit in one per CU and 3 (68 KB, two per CU)
 // beyond.  kOvDecodeChain = 3 forces it wherever it fits, 1 and 2 keep it
 // off.
@@ -613,7 +618,7 @@ int decode_token_stages(int T, int d, int N, int E, int k) {
   const int ov = override_value(kOvDecodeChain);
   if (ov == 1 || ov == 2) return 0;
   if (k > 8 || N % 16 != 0 || d % 64 != 0) return 0;
-  if (ov != 3 && (long long)T * k > 64) return 0;
+  if (ov != 3 && (long long)T * k > 48) return 0;
   if (k > 4) return tok_smem<2, 3>(d) <= 160 * 1024 ? 3 : 0;
   const int st = (long long)T * (N / 16) <= 256 ? 4 : 3;
   if (st == 4 && tok_smem<1, 4>(d) <= 160 * 1024) return 4;

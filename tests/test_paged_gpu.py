@@ -77,7 +77,7 @@ CASES = [
     (64, 2560, 64, 4, 8, 128, 12, 16, "decode"),
     (64, 2560, 64, 4, 8, 128, 12, 16, "grouped"),
     (37, 256, 16, 4, 2, 64, 5, 8, "decode"),
-    (8, 2560, 64, 4, 8, 128, 12, 16, "decode"),   # token-major decode kernel (T * k <= 64)
+    (8, 2560, 64, 4, 8, 128, 12, 16, "decode"),   # token-major decode kernel (T * k <= 48)
     (3, 256, 16, 4, 2, 64, 5, 8, "decode"),
     (300, 512, 32, 4, 4, 64, 40, 16, "grouped"),
     (1000, 256, 8, 2, 1, 64, 1100, 1, "grouped"),

@@ -46,7 +46,7 @@ def with_path(path, fn):
 
 SHAPES = [
     # T, d, E, k, H, D
-    (8, 2560, 64, 4, 8, 128),      # token-major decode kernel (T * k <= 64)
+    (8, 2560, 64, 4, 8, 128),      # token-major decode kernel (T * k <= 48)
     (5, 256, 8, 3, 2, 32),
     (37, 256, 8, 2, 2, 32),
     (64, 2560, 64, 4, 8, 128),
