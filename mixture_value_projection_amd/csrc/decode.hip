@@ -676,9 +676,11 @@ hipError_t launch_decode_token(const DecodeTokenArgs& a, int stages, hipStream_t
 // T * k up to which it is the default, measured: the value experts (d =
 // 2560, N = 1024) at T = 1, 2, 4, 8 took 16.1 / 20.1 / 30.5 / 50.4 us against
 // 33.8 / 35.3 / 37.4 and 43.7 us for the streaming kernel with one column
-// group per wave; the FFN (100 experts of width 768, top-8) at T = 1, 2, 4, 8
-// 62 / 89 / 133 / 186 us against 114 / 125 / 150 / 175 us.
-static int chain_auto_pairs(int mode) { return mode == kGemmRoutedSilu ? 16 : 32; }
+// group per wave; the FFN (100 experts of width 768, top-8) at T = 1, 2, 3, 4
+// 57 / 83 / 109 / 129 us against 94 / 103 / 114 / 121 us for the streaming
+// kernels with their non-temporal row loads (before those loads, T = 4 took
+// 150 us there, and the chain kernel was the default up to 32 pairs).
+static int chain_auto_pairs(int mode) { return mode == kGemmRoutedSilu ? 16 : 24; }
 static int chain_waves(int mode) { return mode == kGemmRoutedSwiGLU ? 8 : 4; }
 static int chain_steps_per_wave(const DecodeArgs& a) {
   // 1 / 2 force it on / off (tests, measurement); 3 forces the token-major kernel.
