@@ -85,3 +85,52 @@ def test_noalloc_refuses_calls_beyond_its_scratch():
         binding.value_forward_noalloc(x, rw, None, ew, sh.k, sh.scale, out)
     torch.cuda.synchronize()
     assert bool((out == 3.0).all()), "a refused call must leave the output untouched"
+
+
+@pytest.mark.parametrize("name,T,T_other", [("decode", 64, 37), ("prefill", 1024, 300)])
+def test_noalloc_graph_replays(name, T, T_other):
+    """The entry point is meant for code under graph capture: one call
+    captured into a HIP graph, replayed four times with an eager call of
+    another size on the same scratch before each replay, gives the eager
+    call's bits (output and routing) on every replay."""
+    sh = inputs.WORKLOADS[name].shape
+    H, D = sh.n_kv_heads, sh.head_dim
+    say(f"noalloc graph {name}: T={T}, eager T={T_other} between replays")
+    g = P.to_gpu_inputs(inputs.make_workload(name, T=T), DEV)
+    out = torch.empty(T, H, D, dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty(T, sh.k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, sh.k, dtype=torch.float32, device=DEV)
+    xo = g["x"][:T_other].contiguous()
+    out_o = torch.empty(T_other, H, D, dtype=torch.bfloat16, device=DEV)
+
+    def call():
+        binding.value_forward_noalloc(g["x"], g["router_w"], g["router_b"], g["expert_w"], sh.k,
+                                      sh.scale, out, topk_idx=idx, topk_w=w)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = (out.clone(), idx.clone(), w.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        idx.fill_(-7)
+        w.fill_(float("nan"))
+        binding.value_forward_noalloc(xo, g["router_w"], g["router_b"], g["expert_w"], sh.k,
+                                      sh.scale, out_o)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager[0].view(torch.int16)), f"replay {rep}: outputs"
+        assert torch.equal(idx, eager[1]), f"replay {rep}: routing"
+        assert torch.equal(w.view(torch.int32), eager[2].view(torch.int32)), f"replay {rep}: weights"
+    rows = np.random.default_rng(T + 1).choice(T, size=min(T, 128), replace=False)
+    st = P.full_check(g, sh.k, sh.scale, H, D, out, idx, w, tokens=np.sort(rows),
+                      what=f"noalloc graph {name} T={T}")
+    say(f"  four replays bitwise equal to the eager call; oracle {st}")
+    del graph
